@@ -1,0 +1,279 @@
+"""Benchmark: Qwen3-8B-shaped paged attention on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: plan (host) + causal paged prefill of 8 requests x
+4096 tokens (32 q / 8 kv heads, D 128, page 16, pages permuted over a 64K-page
+pool, split 4096) + paged decode of 64 requests with contexts uniform in
+[1, 32768] (split 2048, partial states merged in fixed order).
+
+Prints ONE JSON line. ``value`` is prefill attention TFLOP/s (algorithmic
+FLOPs 4 * D * Hq * sum over rows of visible keys, divided by the prefill
+call's time from HIP events on its stream); ``decode.value`` is decode KV
+GB/s (bytes of K and V read once per kv head, plus q, out, lse and page ids).
+``roofline`` is the prefill kernel against the bf16 MFMA peak,
+``decode.roofline`` the decode kernel against HBM bandwidth. ``cpu_baseline``
+is the float64 CPU oracle timed on a bounded sample of the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s + decode KV GB/s (Qwen3-8B shape), % roofline, bit-invariant"
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "invariant_paged_kv_amd", "csrc", "bia.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+
+
+def prefill_flops(qo_lens, kv_lens, num_qo_heads, head_dim) -> float:
+    """4 * D * Hq * sum over query rows of the keys each row sees (QK^T and
+    PV over visible keys only)."""
+    total = 0
+    for qo, kv in zip(qo_lens, kv_lens):
+        qo, kv = int(qo), int(kv)
+        first = kv - qo + 1            # keys seen by the first query row
+        total += qo * (first + kv) // 2
+    return 4.0 * head_dim * num_qo_heads * total
+
+
+def decode_bytes(kv_lens, num_qo_heads, num_kv_heads, head_dim, page_size=16) -> float:
+    kv = np.asarray(kv_lens, dtype=np.int64)
+    b = kv.sum() * num_kv_heads * head_dim * 2 * 2            # K and V, bf16
+    b += len(kv) * num_qo_heads * head_dim * 2 * 2            # q in, out
+    b += len(kv) * num_qo_heads * 4                           # lse
+    b += 4 * ((kv + page_size - 1) // page_size).sum()         # page ids
+    return float(b)
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if absent or taken on other kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    m = re.search(r"source_sha256_16:\s*(\w+)", text)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(rf"^{kernel}_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+class Timer:
+    """HIP events on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def _oracle_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
+def cpu_baseline_prefill(b):
+    """The float64 CPU oracle on request 0 of the prefill batch (4096 tokens,
+    all 32 q heads): 1/8 of the prefill workload, same inputs."""
+    import oracle
+    import workloads as W
+    q, kp, vp, qo_ip, kv_ip, pt, _ = W.host_subset(b, [0])
+    t = time.perf_counter()
+    oracle.attention_paged(q, kp, vp, qo_ip, kv_ip, pt, b.num_kv_heads, b.sm_scale)
+    dt = time.perf_counter() - t
+    fl = prefill_flops(np.diff(qo_ip), np.diff(kv_ip), b.num_qo_heads, b.head_dim)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": _oracle_threads(), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "prefill request 0 of 8 (4096 tokens, all 32 q heads): 1/8 of "
+                      "the prefill workload, same seeded inputs"}
+
+
+def cpu_baseline_decode(b, n=8):
+    """The float64 CPU oracle on the first ``n`` decode requests."""
+    import oracle
+    import workloads as W
+    reqs = list(range(n))
+    q, kp, vp, qo_ip, kv_ip, pt, _ = W.host_subset(b, reqs)
+    t = time.perf_counter()
+    oracle.decode_paged(q, kp, vp, kv_ip, pt, b.num_kv_heads, b.sm_scale)
+    dt = time.perf_counter() - t
+    by = decode_bytes(np.diff(kv_ip), b.num_qo_heads, b.num_kv_heads, b.head_dim)
+    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s",
+            "cores": _oracle_threads(), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"decode requests 0..{n - 1} of 64 "
+                      f"({int(np.diff(kv_ip).sum())} context tokens), same seeded inputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one "
+              "GPU (one GPU's share of the attention at its real shape); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_paged_kv_amd as bia
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bia.load_library()
+    stream = torch.cuda.current_stream(dev)
+
+    pb = W.qwen_prefill(device=dev)                       # 8 x 4096, 64K-page pool
+    db = W.decode_batch(64, seed=4, num_pages=131072, device=dev)
+    p_pt = torch.as_tensor(pb.page_table, dtype=torch.int32, device=dev)
+    d_pt = torch.as_tensor(db.page_table, dtype=torch.int32, device=dev)
+    p_out = torch.empty_like(pb.q)
+    p_lse = torch.empty(pb.q.shape[:2], dtype=torch.float32, device=dev)
+    d_out = torch.empty_like(db.q)
+    d_lse = torch.empty(db.q.shape[:2], dtype=torch.float32, device=dev)
+    heads = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128)
+
+    def make_plans():
+        pp = bia.bia_plan_create(bia.BIA_MODE_PREFILL, pb.qo_indptr, pb.kv_indptr,
+                                 pb.page_table, num_pages=pb.num_pages,
+                                 split_size=bia.BIA_PREFILL_SPLIT, **heads)
+        dp = bia.bia_plan_create(bia.BIA_MODE_DECODE, db.qo_indptr, db.kv_indptr,
+                                 db.page_table, num_pages=db.num_pages,
+                                 split_size=bia.BIA_DECODE_SPLIT, **heads)
+        return pp, dp
+
+    pp, dp = make_plans()
+    p_ws = torch.empty(max(pp.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    d_ws = torch.empty(max(dp.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    pp.close()
+    dp.close()
+
+    p_timer, d_timer = Timer(torch, stream), Timer(torch, stream)
+    plans_alive = []
+
+    def step(timed: bool):
+        pp, dp = make_plans()                      # a1: plan from the lengths alone
+        plans_alive.append((pp, dp))               # freed after the stream drains
+        s = p_timer.start() if timed else None
+        bia.bia_prefill_paged(pp, pb.q, pb.k_pool, pb.v_pool, p_pt, pb.sm_scale, p_out,
+                              p_lse, p_ws, stream)
+        if timed:
+            p_timer.stop(s)
+            s = d_timer.start()
+        bia.bia_decode_paged(dp, db.q, db.k_pool, db.v_pool, d_pt, db.sm_scale, d_out,
+                             d_lse, d_ws, stream)
+        if timed:
+            d_timer.stop(s)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    ref_p = p_out.clone()
+    ref_d = d_out.clone()
+    for pp, dp in plans_alive:
+        pp.close(), dp.close()
+    plans_alive.clear()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for pp, dp in plans_alive:
+        pp.close(), dp.close()
+
+    invariant = bool(torch.equal(ref_p.view(torch.int16), p_out.view(torch.int16)) and
+                     torch.equal(ref_d.view(torch.int16), d_out.view(torch.int16)))
+
+    p_flops = prefill_flops(pb.qo_lens(), pb.kv_lens(), 32, 128)
+    d_bytes = decode_bytes(db.kv_lens(), 32, 8, 128)
+    p_ms = p_timer.mean_ms()
+    d_ms = d_timer.mean_ms()
+    p_tflops = p_flops / (p_ms * 1e-3) / 1e12
+    d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+
+    p_traffic = read_traffic("prefill")
+    d_traffic = read_traffic("decode")
+    result = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B-shaped attention layer: causal paged prefill 8 x 4096 "
+                        "tokens + paged decode of 64 requests, contexts U[1, 32768]",
+            "num_qo_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
+            "prefill": {"requests": 8, "tokens": 4096, "pool_pages": pb.num_pages,
+                        "split": bia.BIA_PREFILL_SPLIT},
+            "decode": {"requests": 64, "ctx": "uniform [1, 32768]",
+                       "total_kv_tokens": int(db.kv_lens().sum()),
+                       "pool_pages": db.num_pages, "split": bia.BIA_DECODE_SPLIT},
+        },
+        "prefill_ms": round(p_ms, 4),
+        "roofline": {
+            "bound": "mfma", "achieved": round(p_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(p_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": p_traffic,
+        },
+        "decode": {
+            "value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_ms, 4),
+            "roofline": {
+                "bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                "traffic": d_traffic,
+            },
+        },
+        "bit_invariant_across_steps": invariant,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(pb)
+        result["decode"]["cpu_baseline"] = cpu_baseline_decode(db)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * bia.h — batch- and chunk-invariant attention over a paged KV cache, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is causal softmax attention of bf16 queries over
+ * bf16 keys and values stored in fixed-size pages, split along the KV axis
+ * into partitions of a fixed size, with the partial (o, lse) states of the
+ * partitions merged in ascending partition order (sglang PR #10417 "[POC]
+ * Support deterministic inference", Modifications: batch-invariant prefill
+ * and decode, the paged prefill wrapper for every extend, a fixed split-KV of
+ * 2048 tokens for decode and 4096 for prefill). Because the partition, the
+ * merge order and every tile shape depend only on a request's own lengths,
+ * a request's output bits do not depend on the batch it shares, on where its
+ * pages sit in the pool, or on the GPU's compute-unit count; and a chunked
+ * prefill whose chunks start on the 128-row q-tile grid reproduces the
+ * unchunked prefill bit for bit (sglang PR #43612, commit message and
+ * Summary: the fa2 q tile is 128 rows, 128 / gqa_group tokens).
+ *
+ * Conventions shared by every call:
+ *   - B requests. qo_len_r = qo_indptr[r+1] - qo_indptr[r] new query tokens
+ *     attend to kv_len_r = kv_indptr[r+1] - kv_indptr[r] keys, which already
+ *     include this call's own tokens. Query i of request r sits at absolute
+ *     position kv_len_r - qo_len_r + i and sees keys 0 .. that position
+ *     (bottom-right causal alignment, so a chunk attends to its cached prefix).
+ *   - Pages: P = 16 tokens. Request r's pages are
+ *     page_table[page_off_r .. page_off_r + ceil(kv_len_r / P) - 1] with
+ *     page_off_r = sum_{r' < r} ceil(kv_len_r' / P). Token j of request r is
+ *     slot j % P of page page_table[page_off_r + j / P].
+ *   - K and V pools: bf16 [num_pages][P][Hkv][D], row-major, separate buffers.
+ *   - q / out: bf16 [sum qo_len][Hq][D] (requests packed in order); lse: fp32
+ *     [sum qo_len][Hq], natural log of sum_j exp(s_j), s_j = sm_scale * q.k_j.
+ *   - GQA: q head h reads kv head h / (Hq / Hkv).
+ *   - Memory in the pools outside the request's keys (other pages, slots past
+ *     kv_len in the last page) is never read into a result and may hold
+ *     anything, NaN included.
+ *
+ * Ownership: the caller owns every device buffer (q, pools, page table, out,
+ * lse, workspace); the library owns the plan (host memory plus a pinned host
+ * copy of its work list). Run calls are asynchronous on `stream` (a
+ * hipStream_t; NULL means the null stream), never synchronise the host, and
+ * copy the plan's work list into the head of the workspace with
+ * hipMemcpyAsync, so the plan and the workspace must stay alive until the
+ * stream has passed the call, and one workspace must not serve two calls that
+ * can overlap.
+ *
+ * Errors: every call returns a bia_status; nothing is thrown across the ABI.
+ * Arguments are checked before anything is enqueued. bia_last_error() gives a
+ * thread-local message for the last non-OK status on the calling thread.
+ */
+#ifndef BIA_H_
+#define BIA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bia_status {
+  BIA_OK = 0,
+  BIA_ERR_INVALID_ARG = 1, /* null pointer, bad mode, bad split size, ...   */
+  BIA_ERR_SHAPE = 2,       /* indptr not monotone, qo_len > kv_len, ...      */
+  BIA_ERR_PAGE_RANGE = 3,  /* a page id outside [0, num_pages)               */
+  BIA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the plan's   */
+  BIA_ERR_UNSUPPORTED = 5, /* head_dim, page size or GQA group not built    */
+  BIA_ERR_HIP = 6          /* a HIP runtime call failed                      */
+} bia_status;
+
+typedef enum bia_mode {
+  BIA_MODE_PREFILL = 0, /* any qo_len_r in [0, kv_len_r]                   */
+  BIA_MODE_DECODE = 1   /* qo_len_r == 1 for every request                 */
+} bia_mode;
+
+/* Default split-KV partition sizes (sglang PR #10417, Modifications). */
+#define BIA_PREFILL_SPLIT 4096
+#define BIA_DECODE_SPLIT 2048
+/* Rows of the prefill q tile; rows are (token, head-in-group) pairs packed
+ * token-major, so one tile holds 128 / (Hq / Hkv) tokens of one kv head. */
+#define BIA_Q_TILE_ROWS 128
+/* Keys per KV tile; a split size must be a positive multiple of it. */
+#define BIA_KV_TILE 64
+#define BIA_PAGE_SIZE 16
+
+typedef struct bia_plan bia_plan; /* opaque, library-owned */
+
+/*
+ * Build the work list of one prefill or decode call from the batch's lengths
+ * alone (sglang PR #43612, Summary: the probe drives a paged prefill wrapper
+ * planned with fixed_split_size; the split is a pure kernel knob).
+ *
+ *   qo_indptr, kv_indptr: host int32 [batch + 1], start at 0, non-decreasing,
+ *       0 <= qo_len_r <= kv_len_r; in decode mode qo_len_r == 1.
+ *   page_table: host int32 [sum ceil(kv_len_r / page_size)]; only checked
+ *       (every id in [0, num_pages)); the run call reads the device copy,
+ *       which must hold the same ids. May be NULL when no request has keys.
+ *   num_qo_heads % num_kv_heads == 0 with a group of 1, 2, 4 or 8;
+ *   head_dim 64 or 128; page_size 16;
+ *   split_size > 0 and a multiple of BIA_KV_TILE (BIA_PREFILL_SPLIT /
+ *       BIA_DECODE_SPLIT for the pages' setting). Keys of request r are cut
+ *       into partitions [k * split_size, (k + 1) * split_size), anchored at
+ *       key 0 of the request.
+ * On success *out_plan receives a plan to free with bia_plan_destroy. The
+ * arrays are not retained. batch == 0 gives an empty plan whose runs do
+ * nothing.
+ */
+bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, const int32_t* page_table,
+                           int32_t batch, int32_t num_qo_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t num_pages,
+                           int32_t split_size, bia_plan** out_plan);
+
+/* Bytes of device workspace a run of this plan needs (0 for NULL). */
+size_t bia_plan_workspace_bytes(const bia_plan* plan);
+
+/* Free a plan. Only once every run enqueued with it has completed. NULL is a
+ * no-op. */
+void bia_plan_destroy(bia_plan* plan);
+
+/*
+ * Causal prefill of a BIA_MODE_PREFILL plan (sglang PR #43612, Summary;
+ * sglang PR #10417, Modifications).
+ *   q: device bf16 [sum qo_len][Hq][D]; k_pool, v_pool: device bf16
+ *   [num_pages][16][Hkv][D]; page_table_dev: device int32, same ids as the
+ *   plan's; out: device bf16 [sum qo_len][Hq][D]; lse: device fp32
+ *   [sum qo_len][Hq] or NULL to skip it; workspace: device, at least
+ *   bia_plan_workspace_bytes(plan) bytes, 256-byte aligned.
+ * Output bits of a request depend only on its q, its keys and values, its
+ * qo_len, kv_len, split_size and sm_scale.
+ */
+bia_status bia_prefill_paged(const bia_plan* plan, const void* q,
+                             const void* k_pool, const void* v_pool,
+                             const int32_t* page_table_dev, float sm_scale,
+                             void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Decode of a BIA_MODE_DECODE plan: one query token per request attends to
+ * all kv_len_r keys (sglang PR #10417, Modifications: batch-invariant decode
+ * with a fixed split of 2048).
+ *   q, out: device bf16 [batch][Hq][D]; lse: device fp32 [batch][Hq] or NULL;
+ *   other arguments as for bia_prefill_paged.
+ */
+bia_status bia_decode_paged(const bia_plan* plan, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* page_table_dev, float sm_scale,
+                            void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Merge partial attention states in a fixed order: row i folds states
+ * state_indptr[i] .. state_indptr[i+1]-1 in ascending order. A state with
+ * lse = -inf is empty and skipped; the rest combine as
+ *   M = max lse_k, w_k = exp(lse_k - M), o = sum w_k o_k / sum w_k,
+ *   lse = M + log sum w_k
+ * (the fixed-order merge of split-KV partial states, sglang PR #10417,
+ * Modifications). A row with only empty states gives o = 0, lse = -inf. The
+ * prefill and decode calls fold their own partitions with the same function.
+ *   v: device fp32 [n_states][num_heads][head_dim]; s: device fp32
+ *   [n_states][num_heads]; state_indptr_dev: device int32 [n_rows + 1];
+ *   out: device bf16 [n_rows][num_heads][head_dim]; out_lse: device fp32
+ *   [n_rows][num_heads] or NULL. head_dim 64 or 128. The indptr is read on
+ *   the device only and must start at 0 and be non-decreasing with its last
+ *   entry <= n_states (not checked).
+ */
+bia_status bia_merge_states(const float* v, const float* s,
+                            const int32_t* state_indptr_dev, int32_t n_rows,
+                            int32_t num_heads, int32_t head_dim, void* out,
+                            float* out_lse, void* stream);
+
+/* Chunk alignment, in tokens, under which a chunked prefill reproduces the
+ * unchunked one bit for bit: 128 (the PREFILL_Q_TILE_TOKENS = 128 constant of
+ * sglang PR #43612, Summary). Chunk starts that are multiples of it land on
+ * the q-tile grid for every GQA group the library supports. */
+int32_t bia_prefill_chunk_align(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* bia_last_error(void);
+
+/* Host-side introspection of a plan's work list, for tests and tools.
+ * bia_plan_num_items: number of compute work items (workgroups launched).
+ * bia_plan_get_items: copies min(n, num_items) items of 8 int32 each:
+ *   {q_row0, n_tok, pos0, kv_len, page_off, kv_head, kv_begin, state}
+ *   in launch order (see the workspace layout in the library source).
+ * bia_plan_num_states: partial (o, lse) states the plan writes before its
+ *   merge (0 when every row has a single partition). */
+int32_t bia_plan_num_items(const bia_plan* plan);
+int32_t bia_plan_get_items(const bia_plan* plan, int32_t* items, int32_t n);
+int64_t bia_plan_num_states(const bia_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIA_H_ */

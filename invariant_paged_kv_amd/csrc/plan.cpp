@@ -1,0 +1,232 @@
+// Host split planner: validates a batch and lays out its work list.
+//
+// The layout is a function of each request's (qo_len, kv_len) alone: q tiles
+// start at the request's first query token and hold 128 / group tokens;
+// split-KV partitions are [k * split, (k + 1) * split) anchored at key 0 of
+// the request (a fixed split size, sglang PR #10417, Modifications; the
+// 128-row q-tile grid, sglang PR #43612, Summary). The launch order of the
+// items (longest first) changes nothing in any result.
+//
+// Plain C++: no HIP call, so it runs and is tested without a GPU.
+#include <algorithm>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "plan.h"
+
+namespace bia {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+bia_status fail(bia_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Keys of a work item: [kv_begin, min(kv_begin + split, last_pos + 1)).
+static int64_t item_tiles(const WorkItem& w, int32_t split) {
+  int64_t last = static_cast<int64_t>(w.pos0) + w.n_tok - 1;
+  int64_t end = std::min<int64_t>(static_cast<int64_t>(w.kv_begin) + split, last + 1);
+  return ceil_div(end - w.kv_begin, kKvTile);
+}
+
+static bia_status build(PlanData& d, const int32_t* qo_indptr,
+                        const int32_t* kv_indptr) {
+  const bool decode = d.mode == BIA_MODE_DECODE;
+  const int32_t g = d.group;
+  const int32_t T = decode ? 1 : d.tile_tokens;
+  int64_t page_off = 0;
+  for (int32_t r = 0; r < d.batch; ++r) {
+    const int32_t qo_len = qo_indptr[r + 1] - qo_indptr[r];
+    const int32_t kv_len = kv_indptr[r + 1] - kv_indptr[r];
+    for (int32_t t0 = 0; t0 < qo_len; t0 += T) {
+      const int32_t n_tok = std::min(T, qo_len - t0);
+      const int32_t pos0 = kv_len - qo_len + t0;
+      const int64_t last = static_cast<int64_t>(pos0) + n_tok - 1;
+      const int32_t n_splits = static_cast<int32_t>(last / d.split + 1);
+      const int32_t rows = n_tok * g;
+      for (int32_t h = 0; h < d.num_kv_heads; ++h) {
+        int64_t base = -1;
+        if (n_splits > 1) {
+          base = d.n_states;
+          d.n_states += static_cast<int64_t>(n_splits) * rows;
+          if (d.n_states > INT32_MAX)
+            return fail(BIA_ERR_SHAPE, "plan needs %lld partial states (> 2^31)",
+                        static_cast<long long>(d.n_states));
+          d.merges.push_back(MergeItem{static_cast<int32_t>(base), n_splits,
+                                       qo_indptr[r] + t0, n_tok, h, rows, 0, 0});
+        }
+        for (int32_t k = 0; k < n_splits; ++k) {
+          WorkItem w{qo_indptr[r] + t0, n_tok, pos0, kv_len,
+                     static_cast<int32_t>(page_off), h, k * d.split,
+                     base < 0 ? -1 : static_cast<int32_t>(base + int64_t(k) * rows)};
+          d.items.push_back(w);
+        }
+      }
+    }
+    page_off += ceil_div(kv_len, d.page_size);
+  }
+  if (d.items.size() > static_cast<size_t>(INT32_MAX))
+    return fail(BIA_ERR_SHAPE, "too many work items");
+  // Longest items first, so the tail of the launch is short work; a stable
+  // sort keeps the plan itself deterministic.
+  const int32_t split = d.split;
+  std::stable_sort(d.items.begin(), d.items.end(),
+                   [split](const WorkItem& a, const WorkItem& b) {
+                     return item_tiles(a, split) > item_tiles(b, split);
+                   });
+  return BIA_OK;
+}
+
+}  // namespace bia
+
+using namespace bia;
+
+extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
+                                      const int32_t* kv_indptr,
+                                      const int32_t* page_table, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size,
+                                      int32_t num_pages, int32_t split_size,
+                                      bia_plan** out_plan) {
+  if (out_plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out_plan is NULL");
+  *out_plan = nullptr;
+  if (mode != BIA_MODE_PREFILL && mode != BIA_MODE_DECODE)
+    return fail(BIA_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
+  if (batch < 0) return fail(BIA_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
+    return fail(BIA_ERR_INVALID_ARG, "qo_indptr / kv_indptr is NULL");
+  if (num_qo_heads <= 0 || num_kv_heads <= 0)
+    return fail(BIA_ERR_INVALID_ARG, "head counts must be positive (%d, %d)",
+                num_qo_heads, num_kv_heads);
+  if (num_qo_heads % num_kv_heads != 0)
+    return fail(BIA_ERR_SHAPE, "num_qo_heads %d is not a multiple of num_kv_heads %d",
+                num_qo_heads, num_kv_heads);
+  const int32_t group = num_qo_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(BIA_ERR_UNSUPPORTED, "GQA group %d not supported (1, 2, 4, 8)", group);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(BIA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  if (page_size != kPageSize)
+    return fail(BIA_ERR_UNSUPPORTED, "page_size %d not supported (16)", page_size);
+  if (num_pages < 0) return fail(BIA_ERR_INVALID_ARG, "num_pages %d < 0", num_pages);
+  if (split_size <= 0 || split_size % kKvTile != 0)
+    return fail(BIA_ERR_INVALID_ARG,
+                "split_size %d must be a positive multiple of the %d-key KV tile",
+                split_size, kKvTile);
+
+  int64_t total_pages = 0;
+  if (batch > 0) {
+    if (qo_indptr[0] != 0 || kv_indptr[0] != 0)
+      return fail(BIA_ERR_SHAPE, "indptr arrays must start at 0");
+    for (int32_t r = 0; r < batch; ++r) {
+      const int64_t qo = int64_t(qo_indptr[r + 1]) - qo_indptr[r];
+      const int64_t kv = int64_t(kv_indptr[r + 1]) - kv_indptr[r];
+      if (qo < 0 || kv < 0)
+        return fail(BIA_ERR_SHAPE, "request %d: indptr decreases", r);
+      if (qo > kv)
+        return fail(BIA_ERR_SHAPE, "request %d: qo_len %lld > kv_len %lld", r,
+                    static_cast<long long>(qo), static_cast<long long>(kv));
+      if (mode == BIA_MODE_DECODE && qo != 1)
+        return fail(BIA_ERR_SHAPE, "request %d: decode needs qo_len 1, got %lld", r,
+                    static_cast<long long>(qo));
+      total_pages += ceil_div(kv, page_size);
+    }
+    if (total_pages > 0 && page_table == nullptr)
+      return fail(BIA_ERR_INVALID_ARG, "page_table is NULL");
+    for (int64_t i = 0; i < total_pages; ++i) {
+      if (page_table[i] < 0 || page_table[i] >= num_pages)
+        return fail(BIA_ERR_PAGE_RANGE, "page_table[%lld] = %d outside [0, %d)",
+                    static_cast<long long>(i), page_table[i], num_pages);
+    }
+    if (total_pages > INT32_MAX)
+      return fail(BIA_ERR_SHAPE, "page table longer than 2^31 entries");
+  }
+
+  bia_plan* plan = new (std::nothrow) bia_plan();
+  if (plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out of host memory");
+  PlanData& d = plan->d;
+  d.mode = mode;
+  d.batch = batch;
+  d.num_qo_heads = num_qo_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = head_dim;
+  d.page_size = page_size;
+  d.num_pages = num_pages;
+  d.split = split_size;
+  d.group = group;
+  d.tile_tokens = kQTileRows / group;
+  d.total_q = batch > 0 ? qo_indptr[batch] : 0;
+  d.n_states = 0;
+  bia_status st = BIA_OK;
+  try {
+    st = build(d, qo_indptr, kv_indptr);
+  } catch (const std::bad_alloc&) {
+    st = fail(BIA_ERR_INVALID_ARG, "out of host memory while planning");
+  }
+  if (st != BIA_OK) {
+    delete plan;
+    return st;
+  }
+  d.off_items = 0;
+  d.off_merges = d.items.size() * sizeof(WorkItem);
+  d.blob_bytes = d.off_merges + d.merges.size() * sizeof(MergeItem);
+  d.off_o = align_up(d.blob_bytes, kWsAlign);
+  d.off_lse = align_up(d.off_o + size_t(d.n_states) * head_dim * sizeof(float), kWsAlign);
+  d.ws_bytes = d.n_states > 0 ? d.off_lse + size_t(d.n_states) * sizeof(float)
+                              : align_up(d.blob_bytes, kWsAlign);
+  d.blob.resize(d.blob_bytes);
+  if (!d.items.empty())
+    std::memcpy(d.blob.data() + d.off_items, d.items.data(),
+                d.items.size() * sizeof(WorkItem));
+  if (!d.merges.empty())
+    std::memcpy(d.blob.data() + d.off_merges, d.merges.data(),
+                d.merges.size() * sizeof(MergeItem));
+  *out_plan = plan;
+  return BIA_OK;
+}
+
+extern "C" size_t bia_plan_workspace_bytes(const bia_plan* plan) {
+  return plan == nullptr ? 0 : plan->d.ws_bytes;
+}
+
+extern "C" int32_t bia_plan_num_items(const bia_plan* plan) {
+  return plan == nullptr ? 0 : static_cast<int32_t>(plan->d.items.size());
+}
+
+extern "C" int32_t bia_plan_get_items(const bia_plan* plan, int32_t* items, int32_t n) {
+  if (plan == nullptr || items == nullptr || n <= 0) return 0;
+  const int32_t m = std::min<int32_t>(n, static_cast<int32_t>(plan->d.items.size()));
+  std::memcpy(items, plan->d.items.data(), size_t(m) * sizeof(WorkItem));
+  return m;
+}
+
+extern "C" int64_t bia_plan_num_states(const bia_plan* plan) {
+  return plan == nullptr ? 0 : plan->d.n_states;
+}
+
+extern "C" int32_t bia_prefill_chunk_align(void) { return kQTileRows; }
+
+extern "C" const char* bia_last_error(void) { return g_last_error.c_str(); }

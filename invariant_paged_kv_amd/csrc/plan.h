@@ -1,0 +1,70 @@
+// Internal plan structures shared by the host planner (plan.cpp, plain C++)
+// and the launch layer (bia.hip).
+#ifndef BIA_PLAN_INTERNAL_H_
+#define BIA_PLAN_INTERNAL_H_
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "bia.h"
+
+namespace bia {
+
+// One workgroup's work: one q tile of one kv head of one request, over one
+// split-KV partition. For decode a "tile" is the single query token.
+//   q_row0   global index (into q / out) of the tile's first query token
+//   n_tok    query tokens in the tile (<= 128 / group; ragged last tile)
+//   pos0     absolute KV position of the tile's first token
+//   kv_len   the request's key count
+//   page_off index in the page table of the request's first page
+//   kv_head  kv head (its q heads are kv_head * group .. + group - 1)
+//   kv_begin first key of the partition (a multiple of the split size)
+//   state    -1: the tile's rows have one partition, write out/lse directly;
+//            >= 0: first partial-state slot of this (tile, partition); row x
+//            of the tile (x = token * group + head-in-group) uses slot
+//            state + x.
+struct WorkItem {
+  int32_t q_row0, n_tok, pos0, kv_len, page_off, kv_head, kv_begin, state;
+};
+
+// Fixed-order merge of a tile whose rows span several partitions: row x
+// folds slots state0 + k * stride + x for k = 0 .. n_splits - 1, ascending.
+struct MergeItem {
+  int32_t state0, n_splits, q_row0, n_tok, kv_head, stride, pad0, pad1;
+};
+
+static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
+static_assert(sizeof(MergeItem) == 32, "merge item is 8 int32");
+
+constexpr int kQTileRows = BIA_Q_TILE_ROWS;
+constexpr int kKvTile = BIA_KV_TILE;
+constexpr int kPageSize = BIA_PAGE_SIZE;
+constexpr size_t kWsAlign = 256;
+
+struct PlanData {
+  bia_mode mode;
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages;
+  int32_t split, group, tile_tokens;
+  int64_t total_q;   // sum of qo_len: rows of q / out
+  int64_t n_states;  // partial states written before the merge
+  std::vector<WorkItem> items;
+  std::vector<MergeItem> merges;
+  // Workspace layout (byte offsets): [items | merges] (the uploaded blob),
+  // then fp32 o[n_states][head_dim], then fp32 lse[n_states].
+  size_t off_items, off_merges, off_o, off_lse, blob_bytes, ws_bytes;
+  std::vector<unsigned char> blob;  // host copy of [items | merges]
+};
+
+void set_error(const char* fmt, ...);
+bia_status fail(bia_status st, const char* fmt, ...);
+
+}  // namespace bia
+
+// The opaque handle of the C ABI.
+struct bia_plan {
+  bia::PlanData d;
+  void* pinned = nullptr;  // pinned copy of d.blob, made by the launch layer
+};
+
+#endif  // BIA_PLAN_INTERNAL_H_

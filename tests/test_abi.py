@@ -1,0 +1,224 @@
+"""C-ABI library on the CPU: it loads, exports what bia.h declares, validates
+its arguments before any launch, and plans work lists whose layout depends on
+each request's own lengths only. No kernel runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import invariant_paged_kv_amd as bia
+from invariant_paged_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bia.h")
+
+QWEN = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bia_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = bia.load_library()
+    names = declared_functions()
+    assert "bia_prefill_paged" in names and "bia_merge_states" in names
+    for name in names:
+        assert hasattr(lib, name), f"libbia.so does not export {name}"
+
+
+def test_python_binding_has_every_entry_point():
+    """The binding keeps the C names of the calls a user makes."""
+    for name in ["bia_plan_create", "bia_plan_destroy", "bia_plan_workspace_bytes",
+                 "bia_prefill_paged", "bia_decode_paged", "bia_merge_states",
+                 "bia_prefill_chunk_align", "bia_last_error"]:
+        assert name in declared_functions()
+        assert callable(getattr(bia, name)), name
+
+
+def test_chunk_align_is_128():
+    assert bia.bia_prefill_chunk_align() == 128
+
+
+def plan(mode=bia.BIA_MODE_PREFILL, qo=(0, 100, 400), kv=(0, 100, 400), pt=None,
+         heads=dict(num_qo_heads=4, num_kv_heads=1, head_dim=64), num_pages=64,
+         split=4096):
+    if pt is None:
+        kvl = np.diff(kv)
+        pt = np.arange(int(((kvl + 15) // 16).sum()))
+    return bia.bia_plan_create(mode, qo, kv, pt, num_pages=num_pages, split_size=split,
+                               **heads)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(qo=(0, 5, 3), kv=(0, 10, 20)), "BIA_ERR_SHAPE"),        # qo decreases
+    (dict(qo=(1, 5), kv=(0, 10)), "BIA_ERR_SHAPE"),               # does not start at 0
+    (dict(qo=(0, 11), kv=(0, 10)), "BIA_ERR_SHAPE"),              # qo_len > kv_len
+    (dict(qo=(0, 1), kv=(0, 10), pt=[0]), None),                  # fine (1 page)
+    (dict(qo=(0, 1), kv=(0, 10), pt=[64]), "BIA_ERR_PAGE_RANGE"),
+    (dict(qo=(0, 1), kv=(0, 10), pt=[-1]), "BIA_ERR_PAGE_RANGE"),
+    (dict(split=100), "BIA_ERR_INVALID_ARG"),                     # not a multiple of 64
+    (dict(split=0), "BIA_ERR_INVALID_ARG"),
+    (dict(heads=dict(num_qo_heads=4, num_kv_heads=1, head_dim=96)), "BIA_ERR_UNSUPPORTED"),
+    (dict(heads=dict(num_qo_heads=6, num_kv_heads=4, head_dim=64)), "BIA_ERR_SHAPE"),
+    (dict(heads=dict(num_qo_heads=48, num_kv_heads=3, head_dim=64)), "BIA_ERR_UNSUPPORTED"),
+    (dict(mode=bia.BIA_MODE_DECODE), "BIA_ERR_SHAPE"),            # decode needs qo_len 1
+    (dict(mode=7), "BIA_ERR_INVALID_ARG"),
+])
+def test_plan_validation(kwargs, status):
+    if status is None:
+        plan(**kwargs).close()
+        return
+    with pytest.raises(bia.BiaError) as e:
+        plan(**kwargs)
+    assert str(e.value).startswith(status), str(e.value)
+    assert bia.bia_last_error()
+
+
+def test_null_pointers_rejected_before_anything_runs():
+    lib = bia.load_library()
+    h = ctypes.c_void_p()
+    assert lib.bia_plan_create(0, None, None, None, 2, 4, 1, 64, 16, 64, 4096,
+                               ctypes.byref(h)) == 1
+    assert lib.bia_plan_create(0, None, None, None, 0, 4, 1, 64, 16, 64, 4096,
+                               None) == 1
+    # run calls with a NULL plan fail in the argument check (no HIP call)
+    assert lib.bia_prefill_paged(None, None, None, None, None, 1.0, None, None, None, 0,
+                                 None) == 1
+    assert lib.bia_decode_paged(None, None, None, None, None, 1.0, None, None, None, 0,
+                                None) == 1
+    assert lib.bia_merge_states(None, None, None, 4, 2, 96, None, None, None) == 5
+    assert lib.bia_merge_states(None, None, None, 4, 2, 64, None, None, None) == 1
+    assert lib.bia_merge_states(None, None, None, 0, 2, 64, None, None, None) == 0
+    lib.bia_plan_destroy(None)
+
+
+def test_empty_batch_plan():
+    p = bia.bia_plan_create(bia.BIA_MODE_PREFILL, [0], [0], None, num_pages=0,
+                            split_size=4096, **QWEN)
+    assert p.num_items == 0 and p.num_states == 0
+    p.close()
+
+
+def test_run_rejects_wrong_mode_and_small_workspace():
+    lib = bia.load_library()
+    p = plan()
+    # decode call on a prefill plan: rejected in the argument check
+    st = lib.bia_decode_paged(ctypes.c_void_p(p.handle), None, None, None, None, 1.0, None,
+                              None, None, 0, None)
+    assert st == 1 and "mode" in bia.bia_last_error()
+    dummy = ctypes.c_void_p(256)
+    st = lib.bia_prefill_paged(ctypes.c_void_p(p.handle), dummy, dummy, dummy, dummy, 1.0,
+                               dummy, None, dummy, p.workspace_bytes - 1, None)
+    assert st == 4, bia.bia_last_error()
+    st = lib.bia_prefill_paged(ctypes.c_void_p(p.handle), dummy, dummy, dummy, dummy,
+                               float("nan"), dummy, None, dummy, p.workspace_bytes, None)
+    assert st == 1
+    p.close()
+
+
+# ------------------------------------------------------------ work lists ---
+
+FIELDS = ["q_row0", "n_tok", "pos0", "kv_len", "page_off", "kv_head", "kv_begin", "state"]
+
+
+def items_of(p):
+    return [dict(zip(FIELDS, map(int, row))) for row in p.items()]
+
+
+def request_layout(p, q_row0, kv_head=0):
+    """Items of the request whose first query row is q_row0, as
+    (tile token offset, n_tok, pos0, kv_begin), sorted."""
+    out = []
+    for it in items_of(p):
+        if it["kv_head"] == kv_head and it["q_row0"] >= q_row0:
+            out.append(it)
+    return out
+
+
+def test_tiny_prefill_item_count_and_tiles():
+    p = plan()
+    its = items_of(p)
+    # group 4 -> 32 tokens per tile: ceil(100/32) + ceil(300/32) = 4 + 10
+    assert len(its) == 14
+    assert all(it["state"] == -1 for it in its)  # one partition each at split 4096
+    assert max(it["n_tok"] for it in its) == 32
+    tok = sorted((it["q_row0"], it["n_tok"]) for it in its)
+    covered = []
+    for r0, n in tok:
+        covered.extend(range(r0, r0 + n))
+    assert covered == list(range(400))
+
+
+@pytest.mark.parametrize("split", [64, 128, 4096])
+def test_partitions_anchor_at_key_zero(split):
+    p = plan(split=split)
+    for it in items_of(p):
+        assert it["kv_begin"] % split == 0
+        last = it["pos0"] + it["n_tok"] - 1
+        assert it["kv_begin"] <= last  # never an item with no visible key
+    # every (tile, head) covers partitions 0..floor(last/split) exactly once
+    seen = {}
+    for it in items_of(p):
+        key = (it["q_row0"], it["kv_head"])
+        seen.setdefault(key, []).append(it["kv_begin"] // split)
+    for (r0, h), parts in seen.items():
+        its = [i for i in items_of(p) if i["q_row0"] == r0 and i["kv_head"] == h]
+        last = its[0]["pos0"] + its[0]["n_tok"] - 1
+        assert sorted(parts) == list(range(last // split + 1))
+
+
+def test_request_layout_independent_of_batch():
+    """A request's items (relative to its own rows) are the same alone and in
+    a batch with others, in any position."""
+    def rel(p, r0, base_page):
+        return sorted((it["q_row0"] - r0, it["n_tok"], it["pos0"], it["kv_len"],
+                       it["page_off"] - base_page, it["kv_head"], it["kv_begin"])
+                      for it in items_of(p) if r0 <= it["q_row0"] < r0 + 1000
+                      and it["kv_len"] == 1000)
+    alone = plan(qo=(0, 1000), kv=(0, 1000), split=256, heads=QWEN, num_pages=4096)
+    mixed = plan(qo=(0, 7, 1007, 1050), kv=(0, 33, 1033, 1500), split=256, heads=QWEN,
+                 num_pages=4096)
+    assert rel(alone, 0, 0) == rel(mixed, 7, 3)
+
+
+def test_on_grid_chunk_tiles_are_unchunked_tiles():
+    """A chunk starting on the 128-token grid cuts q tiles exactly where the
+    unchunked call does (same pos0 / n_tok for every tile)."""
+    full = plan(qo=(0, 16384), kv=(0, 16384), split=4096, heads=QWEN, num_pages=1024)
+    tiles_full = {(it["pos0"], it["n_tok"], it["kv_begin"]) for it in items_of(full)}
+    tiles_chunks = set()
+    for c in range(64):
+        ch = plan(qo=(0, 256), kv=(0, 256 * (c + 1)), split=4096, heads=QWEN,
+                  num_pages=1024)
+        tiles_chunks |= {(it["pos0"], it["n_tok"], it["kv_begin"]) for it in items_of(ch)}
+    assert tiles_chunks == tiles_full
+
+
+def test_decode_items_and_states():
+    kv = np.array([1, 2048, 2049, 5000])
+    kvp = np.concatenate([[0], np.cumsum(kv)])
+    p = plan(mode=bia.BIA_MODE_DECODE, qo=np.arange(5), kv=kvp, split=2048, heads=QWEN,
+             num_pages=4096)
+    its = items_of(p)
+    n_splits = [1, 1, 2, 3]
+    assert len(its) == 8 * sum(n_splits)
+    # requests with one partition write directly; the others use g = 4 states
+    # per partition per kv head
+    assert p.num_states == 8 * 4 * (2 + 3)
+    for it in its:
+        r = it["q_row0"]
+        assert it["n_tok"] == 1 and it["pos0"] == kv[r] - 1 and it["kv_len"] == kv[r]
+        assert (it["state"] == -1) == (n_splits[r] == 1)
+
+
+def test_workspace_grows_with_states():
+    a = plan(qo=(0, 1000), kv=(0, 1000), split=4096, heads=QWEN, num_pages=4096)
+    b = plan(qo=(0, 1000), kv=(0, 1000), split=128, heads=QWEN, num_pages=4096)
+    assert a.num_states == 0 and b.num_states > 0
+    assert b.workspace_bytes >= b.num_states * (128 + 1) * 4
+    assert a.workspace_bytes % 256 == 0 and b.workspace_bytes > a.workspace_bytes

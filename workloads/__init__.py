@@ -301,3 +301,27 @@ def mixed_decode_lengths(n: int = 128, seed: int = 5, median: int = 4096,
     rng = np.random.Generator(np.random.PCG64(seed))
     x = np.exp(rng.normal(math.log(median), sigma, size=n))
     return np.clip(np.round(x), 1, cap).astype(np.int64)
+
+
+def host_subset(b: PagedBatch, reqs):
+    """Host copies of the listed requests of a (device) batch: their q rows, a
+    compact pool of just their pages (renumbered 0..n-1 in page-table order)
+    and their indptrs. Renumbering pages does not change what attention
+    computes. Returns (q, k_pool, v_pool, qo_indptr, kv_indptr, page_table,
+    global_rows) where global_rows maps the copied q rows back to ``b.q``."""
+    reqs = [int(r) for r in reqs]
+    counts = pages_needed(b.kv_lens(), b.page_size)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    pages = (np.concatenate([b.page_table[offs[r]:offs[r + 1]] for r in reqs])
+             if reqs else np.zeros(0, dtype=np.int32))
+    idx = torch.as_tensor(pages.astype(np.int64), device=b.k_pool.device)
+    kp = b.k_pool.index_select(0, idx).cpu()
+    vp = b.v_pool.index_select(0, idx).cpu()
+    qo = b.qo_lens()[reqs]
+    kv = b.kv_lens()[reqs]
+    qo_ip = np.concatenate([[0], np.cumsum(qo)]).astype(np.int64)
+    kv_ip = np.concatenate([[0], np.cumsum(kv)]).astype(np.int64)
+    rows = (np.concatenate([np.arange(b.qo_indptr[r], b.qo_indptr[r + 1]) for r in reqs])
+            if reqs else np.zeros(0, dtype=np.int64))
+    q = b.q[torch.as_tensor(rows, device=b.q.device)].cpu()
+    return q, kp, vp, qo_ip, kv_ip, np.arange(len(pages)), rows
