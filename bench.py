@@ -34,7 +34,7 @@ METRIC = "prefill attn TFLOP/s + decode KV GB/s (Qwen3-8B shape), % roofline, bi
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "invariant_paged_kv_amd", "csrc", "bia.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic__qwen3_8b_prefill_8x4096_decode_b64.txt")
 
 
 def prefill_flops(qo_lens, kv_lens, num_qo_heads, head_dim) -> float:
@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy a 1 GiB buffer 3 times, so a counter run also "
+                         "records a plain copy of known size (HBM-byte calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one "
@@ -156,6 +159,13 @@ def main():
     torch.cuda.set_device(dev)
     bia.load_library()
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     pb = W.qwen_prefill(device=dev)                       # 8 x 4096, 64K-page pool
     db = W.decode_batch(64, seed=4, num_pages=131072, device=dev)
