@@ -27,6 +27,7 @@
 #include <cstring>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "bia.h"
 #include "plan.h"
@@ -109,19 +110,58 @@ __device__ __forceinline__ float fold_finish(float M, float sum, float (&acc)[N]
 // softmax is per lane (plus one exchange with lane ^ 32); then O^T += V^T P^T
 // with the probabilities straight from registers as the B operand.
 //
-// LDS: K row-major [64][D + 8] (16-byte row pad: conflict-free 16-byte reads
-// of 32 consecutive rows); V transposed [D][64 + 4] (8-byte pad) so a lane's
-// 8 keys of one d come as two 8-byte reads.
+// Software pipeline (per wave): the score MFMAs of tile j+1 are issued in the
+// same block as the softmax of tile j, so matrix and vector work overlap;
+// K runs one tile ahead of V through single LDS buffers, refilled from
+// registers loaded two tiles ahead from HBM (two barriers per tile).
+//
+// LDS: K and V both row-major, [64][D + 8] and [64][D + 16]. K rows are read
+// 16 bytes per lane (the pad keeps 8 consecutive rows on distinct banks); the
+// V^T operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane i
+// addresses 4 dims of key i / 4, and lane j = 4a + b receives dim 4a + b of
+// those 4 keys (the 32-byte pad keeps the 4 rows on distinct banks).
 //
 // MFMA 32x32x16 layouts (lane l, hi = l / 32, c = l % 32): A[m][k]: m = c,
 // k = 8 hi + e; B[k][n]: n = c, k = 8 hi + e; D[m][n]: n = c,
 // m = 8 (v / 4) + 4 hi + v % 4. The PV contraction uses the key order in
-// which the score MFMA left the probabilities in registers: slot
-// 8 hi + e of (key block kb, half h) is key 32 kb + 16 h + 8 (e / 4) + 4 hi
-// + e % 4; V^T is read in the same order.
+// which the score MFMA left the probabilities in registers: slot 8 hi + e of
+// (key block kb, half h) is key 32 kb + 16 h + 8 (e / 4) + 4 hi + e % 4; V^T
+// is read in the same order.
+//
+// Softmax bookkeeping, all per row and so independent of the tile holding
+// the row: the running max m is raised only when a tile's max exceeds it by
+// more than kLazyMax (base-2 units), so most tiles rescale nothing; scores
+// are scaled inside the exponent (exp2(s * c - m)); masking runs only on
+// tiles that reach past the wave's first row position (elsewhere every key
+// is visible to every row of the wave). The row sum adds the fp32
+// probabilities (summing their bf16 roundings would cost ~1e-3 in lse).
 // ---------------------------------------------------------------------------
+constexpr float kLazyMax = 8.0f;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  // p points into __shared__ memory; the C-style cast moves it to the LDS
+  // address space, which the transposing read requires.
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// max over lanes l and l ^ 32
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(x, fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])),
+                        __builtin_bit_cast(float, static_cast<unsigned>(r[1]))));
+}
+
+#ifndef BIA_PREFILL_MIN_BLOCKS
+#define BIA_PREFILL_MIN_BLOCKS 2
+#endif
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, BIA_PREFILL_MIN_BLOCKS)
 prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                const int32_t* __restrict__ page_table, float scale_log2,
@@ -129,12 +169,12 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
                uint16_t* __restrict__ out, float* __restrict__ lse_out,
                float* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int KS = D + 8;   // bf16 per K row in LDS
-  constexpr int VS = 64 + 4;  // bf16 per V^T row in LDS
+  constexpr int VS = D + 16;  // bf16 per V row in LDS
   constexpr int C = D / 8;    // 16-byte chunks per K/V row
   constexpr int NK = C / 4;   // consecutive keys one thread stages (4 or 2)
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
 
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -148,6 +188,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int hj = x & (g - 1);
   const bool row_valid = tok < it.n_tok;
   const int pos = row_valid ? it.pos0 + tok : -1;
+  // Position of the wave's first row: tiles ending at or before it need no mask.
+  const int wave_pos0 = it.pos0 + ((wave * 32) >> group_shift);
   const int64_t q_off =
       (static_cast<int64_t>(it.q_row0 + tok) * num_qo_heads + it.kv_head * g + hj) * D;
 
@@ -161,113 +203,162 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 
   const int last = it.pos0 + it.n_tok - 1;
   const int kv_end = min(it.kv_begin + split, last + 1);
+  const int n_tiles = (kv_end - it.kv_begin + 63) >> 6;
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
-  const int64_t head_off = static_cast<int64_t>(it.kv_head) * D;
 
-  float m = kNegInf;  // running max, base-2 scaled logits
+  // Staging: this thread moves NK consecutive keys (one page: NK divides 16)
+  // times 8 dims of K and V per tile.
+  const int sc = tid % C;
+  const int skey = (tid / C) * NK;
+  const int64_t thread_off = static_cast<int64_t>(it.kv_head) * D + sc * 8;
+  const int32_t* pt = page_table + it.page_off;
+  uint4 kreg[NK], vreg[NK];
+
+  auto page_of = [&](int t) -> int32_t {
+    const int kk = it.kv_begin + 64 * t + skey;
+    return kk < kv_end ? pt[kk >> 4] : 0;
+  };
+  auto fetch = [&](uint4 (&reg)[NK], const uint16_t* __restrict__ pool, int t,
+                   int64_t page) {
+    const int kk0 = it.kv_begin + 64 * t + skey;
+    const uint16_t* b = pool + (page * 16 + (kk0 & 15)) * slot_stride + thread_off;
+    if (kk0 + NK <= kv_end) {
+#pragma unroll
+      for (int e = 0; e < NK; ++e) reg[e] = *reinterpret_cast<const uint4*>(b + e * slot_stride);
+    } else {  // ragged end of the item: keys at or past kv_end are zero
+#pragma unroll
+      for (int e = 0; e < NK; ++e) {
+        reg[e] = make_uint4(0, 0, 0, 0);
+        if (kk0 + e < kv_end) reg[e] = *reinterpret_cast<const uint4*>(b + e * slot_stride);
+      }
+    }
+  };
+  auto stash_k = [&]() {
+#pragma unroll
+    for (int e = 0; e < NK; ++e)
+      *reinterpret_cast<uint4*>(&k_lds[(skey + e) * KS + sc * 8]) = kreg[e];
+  };
+  auto stash_v = [&]() {
+#pragma unroll
+    for (int e = 0; e < NK; ++e)
+      *reinterpret_cast<uint4*>(&v_lds[(skey + e) * VS + sc * 8]) = vreg[e];
+  };
+  auto scores = [&](f32x16 (&acc)[2]) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(
+            &k_lds[(32 * kb + col) * KS + 16 * s + 8 * hi]);
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw), qf[s],
+                                                          acc[kb], 0, 0, 0);
+      }
+    }
+  };
+  // This lane's base in v_lds for the transposed reads (see the header).
+  const int v_lane = (((lane & 15) >> 2) + 4 * hi) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  float m = kNegInf;  // running max (base-2 scaled logits), possibly stale by < kLazyMax
   float lsum = 0.0f;  // this lane-half's running sum of probabilities
   f32x16 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x16{};
 
-  const int sc = tid % C;   // staging: 16-byte chunk of the row
-  const int skq = tid / C;  // staging: key group (NK consecutive keys)
-
-  for (int t0 = it.kv_begin; t0 < kv_end; t0 += 64) {
-    // ---- stage K (row-major) and V (transposed) of keys t0 .. t0+63 ----
-    uint4 vv[NK];
-#pragma unroll
-    for (int e = 0; e < NK; ++e) {
-      const int kk = t0 + skq * NK + e;
-      uint4 kw = make_uint4(0, 0, 0, 0);
-      uint4 vw = make_uint4(0, 0, 0, 0);
-      if (kk < kv_end) {
-        const int64_t page = page_table[it.page_off + (kk >> 4)];
-        const int64_t off = (page * 16 + (kk & 15)) * slot_stride + head_off + sc * 8;
-        kw = *reinterpret_cast<const uint4*>(kp + off);
-        vw = *reinterpret_cast<const uint4*>(vp + off);
-      }
-      *reinterpret_cast<uint4*>(&k_lds[(skq * NK + e) * KS + sc * 8]) = kw;
-      vv[e] = vw;
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      uint32_t h16[NK];
-#pragma unroll
-      for (int e = 0; e < NK; ++e) {
-        const uint32_t w = (dd >> 1) == 0 ? vv[e].x : (dd >> 1) == 1 ? vv[e].y
-                         : (dd >> 1) == 2 ? vv[e].z : vv[e].w;
-        h16[e] = (dd & 1) ? (w >> 16) : (w & 0xffffu);
-      }
-      uint16_t* dst = &vt_lds[(sc * 8 + dd) * VS + skq * NK];
-      if constexpr (NK == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h16[0] | (h16[1] << 16),
-                                                    h16[2] | (h16[3] << 16));
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = h16[0] | (h16[1] << 16);
-      }
+  // ---- prologue: K(0), V(0) in LDS; S = scores of tile 0; K(1) in LDS;
+  // registers hold K(2) and V(1); page ids for V(2) and K(3) ready ----
+  f32x16 sacc[2];
+  {
+    const int32_t p0 = page_of(0);
+    const int32_t p1 = page_of(1);
+    const int32_t p2 = page_of(2);
+    fetch(kreg, kp, 0, p0);
+    fetch(vreg, vp, 0, p0);
+    stash_k();
+    stash_v();
+    if (n_tiles > 1) {
+      fetch(kreg, kp, 1, p1);
+      fetch(vreg, vp, 1, p1);
     }
     __syncthreads();
+    scores(sacc);
+    __syncthreads();
+    if (n_tiles > 1) stash_k();
+    if (n_tiles > 2) fetch(kreg, kp, 2, p2);
+    __syncthreads();
+  }
+  int32_t page_v = page_of(2);  // page ids for V(j + 2) and K(j + 3)
+  int32_t page_k = page_of(3);
 
-    // ---- S^T = K Q^T for 64 keys x this wave's 32 rows ----
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+  // One tile of the pipeline: softmax of `cur` (tile j) overlapped with the
+  // score MFMAs of tile j+1 into `nxt` (when HasNext), then PV of tile j and
+  // the LDS/register refills for the tiles after it.
+  auto body = [&](auto has_next, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) {
+    constexpr bool kHasNext = decltype(has_next)::value;
+    const int t0 = it.kv_begin + 64 * j;
+    if (t0 + 63 > wave_pos0) {  // wave-uniform: some key is past some row
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kw =
-            *reinterpret_cast<const uint4*>(&k_lds[(32 * kb + col) * KS + 16 * s + 8 * hi]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, kw), qf[s], sacc[kb], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = t0 + 32 * kb + 8 * (v >> 2) + 4 * hi + (v & 3);
+          cur[kb][v] = key <= pos ? cur[kb][v] : kNegInf;
+        }
       }
     }
-
-    // ---- online softmax, one q row per lane ----
-    float sv[2][16];
+    if constexpr (kHasNext) scores(nxt);
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = t0 + 32 * kb + 8 * (v >> 2) + 4 * hi + (v & 3);
-        const float s = sacc[kb][v] * scale_log2;
-        sv[kb][v] = key <= pos ? s : kNegInf;
-        mt = fmaxf(mt, sv[kb][v]);
-      }
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, cur[kb][v]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float alpha = (m_new == m) ? 1.0f : fast_exp2(m - m_new);
-    const float msub = (m_new == kNegInf) ? 0.0f : m_new;
+    mt = max_halves(mt) * scale_log2;
+    const bool raise = mt > m + kLazyMax;  // true on the first tile with a visible key
+    const float m_new = raise ? mt : m;
+    const float alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
     float psum = 0.0f;
     uint32_t pw[2][2][4];  // [kb][half][pair] packed bf16 probabilities
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
-        const float p0 = fast_exp2(sv[kb][v] - msub);
-        const float p1 = fast_exp2(sv[kb][v + 1] - msub);
+        const float p0 = fast_exp2(__builtin_fmaf(cur[kb][v], scale_log2, neg_m));
+        const float p1 = fast_exp2(__builtin_fmaf(cur[kb][v + 1], scale_log2, neg_m));
         psum += p0;
         psum += p1;
         pw[kb][v >> 3][(v & 7) >> 1] = pack_bf16x2(p0, p1);
       }
     }
-    lsum = lsum * alpha + psum;
-    m = m_new;
+    if (__any(raise)) {  // lanes that did not raise have alpha == 1 exactly
+      lsum *= alpha;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+    }
+    lsum += psum;
+    m = m_new;
 
-    // ---- O^T += V^T P^T ----
+    // Every wave is done reading K(j+1), and V(j), stored by all waves after
+    // the previous tile's second barrier, is visible. The last tile needs the
+    // barrier for the second reason alone.
+    __syncthreads();
+    if constexpr (kHasNext) {
+      if (j + 2 < n_tiles) stash_k();
+      if (j + 3 < n_tiles) fetch(kreg, kp, j + 3, page_k);
+    }
+
+    // ---- O^T += V^T P^T (V of tile j) ----
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const uint16_t* vrow = &vt_lds[(32 * b + col) * VS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int kbase = 32 * kb + 16 * h + 4 * hi;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kbase);
-          const uint2 up = *reinterpret_cast<const uint2*>(vrow + kbase + 8);
+          const uint16_t* src = &v_lds[v_lane + (32 * kb + 16 * h) * VS + 32 * b];
+          const uint2 lo = lds_read_tr16(src);
+          const uint2 up = lds_read_tr16(src + 8 * VS);
           const uint4 va = make_uint4(lo.x, lo.y, up.x, up.y);
           const uint4 pb = make_uint4(pw[kb][h][0], pw[kb][h][1], pw[kb][h][2], pw[kb][h][3]);
           o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -275,7 +366,28 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
         }
       }
     }
-    __syncthreads();
+    if constexpr (kHasNext) {
+      __syncthreads();  // every wave is done reading V(j)
+      stash_v();        // V(j+1)
+      if (j + 2 < n_tiles) fetch(vreg, vp, j + 2, page_v);
+      page_v = page_k;
+      page_k = page_of(j + 4);
+    }
+  };
+
+  // Unrolled by two so the score registers alternate without copies; the
+  // last tile has no successor to prefetch.
+  f32x16 sb[2];
+  int j = 0;
+  for (; j + 2 < n_tiles; j += 2) {
+    body(std::true_type{}, sacc, sb, j);
+    body(std::true_type{}, sb, sacc, j + 1);
+  }
+  if (j + 1 < n_tiles) {
+    body(std::true_type{}, sacc, sb, j);
+    body(std::false_type{}, sb, sacc, j + 1);
+  } else {
+    body(std::false_type{}, sacc, sb, j);
   }
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----
@@ -627,8 +739,8 @@ bia_status check_run(const bia_plan* plan, bia_mode mode, const void* q, const v
   if (plan == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->d.mode != mode)
     return bia::fail(BIA_ERR_INVALID_ARG, "plan was made for the other mode");
-  if (!std::isfinite(sm_scale))
-    return bia::fail(BIA_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return bia::fail(BIA_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   if (plan->d.items.empty()) return BIA_OK;
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table_dev == nullptr ||
       out == nullptr)

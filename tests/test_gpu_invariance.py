@@ -41,8 +41,17 @@ def test_prefill_run_to_run_and_relocation():
     say("qwen prefill repeat + page relocation")
     b = W.qwen_prefill(device=DEV, batch=4, length=2048, num_pages=16384)
     o1, l1 = run_prefill(b)
-    o2, l2 = run_prefill(b)
-    assert bits_equal(o1, o2) and bits_equal(l1, l2)
+    for _ in range(4):
+        o2, l2 = run_prefill(b)
+        assert bits_equal(o1, o2) and bits_equal(l1, l2)
+    ragged = W.make_batch([W.Request(77, 300, 403), W.Request(129, 129, 404),
+                           W.Request(500, 1100, 406), W.Request(64, 64, 407)],
+                          num_pages=512, batch_seed=8, device=DEV, **W.QWEN3_8B)
+    for split in (4096, 128):
+        r1, rl1 = run_prefill(ragged, split=split)
+        for _ in range(4):
+            r2, rl2 = run_prefill(ragged, split=split)
+            assert bits_equal(r1, r2) and bits_equal(rl1, rl2)
     moved = W.make_batch(b.requests, num_pages=16384, batch_seed=99, device=DEV,
                          **W.QWEN3_8B)
     assert not np.array_equal(moved.page_table, b.page_table)
