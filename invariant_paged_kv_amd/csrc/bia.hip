@@ -432,12 +432,20 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Decode: one workgroup = one WorkItem = (request, kv head, partition of up to
-// `split` keys), g q heads. The partition's keys go in 32-key chunks to the 4
+// `split` keys), g q heads. The partition's keys go in 16-key chunks to the 4
 // waves round-robin (chunk c -> wave c % 4). In a wave, 8 lanes share one key
-// (each holds D/8 of its dims, so a 16-byte-per-lane load reads whole rows)
-// and 8 keys are in flight per step; the 8 lanes reduce the dot product with
-// three DPP adds. Each 8-lane key group keeps its own online-softmax state;
-// the groups, then the waves, combine in a fixed order at the end.
+// (each holds D/8 of its dims, so 16-byte loads read whole rows) and a lane
+// group takes keys c*16 + ks and c*16 + 8 + ks (one page). Chunks are double
+// buffered in registers: the loads of a wave's next chunk are in flight
+// while the current one is computed, and page ids are read a chunk earlier
+// still.
+//
+// Scores: v_dot2_f32_bf16 partial dots, reduced over the 8 lanes with three
+// DPP adds. PV: the two keys' probabilities (bf16) and the two keys' values
+// of one dim form one v_dot2_f32_bf16, so each dim costs one instruction per
+// key pair. Each 8-lane key group keeps its own online-softmax state (running
+// max raised only past kLazyMax, rescale skipped when no lane raised); the
+// groups, then the waves, combine in a fixed order at the end.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dpp_sum8(float x) {
 #pragma clang fp contract(off)
@@ -478,8 +486,7 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   constexpr int DPL = D / 8;   // dims per lane
   constexpr int W = DPL / 2;   // packed bf16 pairs per lane
   constexpr int U = W / 4;     // 16-byte loads per lane per row
-  constexpr int STEPS = G >= 8 ? 2 : 4;  // keys per key group per chunk
-  constexpr int CHUNK = 8 * STEPS;
+  constexpr int CHUNK = 16;    // keys per wave per chunk
   __shared__ float sm_ml[4][G][2];
   __shared__ float sm_o[4][G][D];
 
@@ -508,6 +515,7 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   const int kv_end = min(it.kv_begin + split, it.kv_len);
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
   const int64_t head_off = static_cast<int64_t>(it.kv_head) * D + part * DPL;
+  const int32_t* pt = page_table + it.page_off;
   float m[G], l[G], o[G][DPL];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -518,19 +526,16 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   }
 
   const int n_chunks = (kv_end - it.kv_begin + CHUNK - 1) / CHUNK;
-  for (int c = wave; c < n_chunks; c += 4) {
-    const int base = it.kv_begin + c * CHUNK;
-    uint32_t kw[STEPS][W], vw[STEPS][W];
+  // page id of this lane group's keys in chunk c (both keys share a page)
+  auto page_of = [&](int c) -> int32_t {
+    const int key = it.kv_begin + CHUNK * c + ks;
+    return (c < n_chunks && key < kv_end) ? pt[key >> 4] : 0;
+  };
+  auto load = [&](uint32_t (&kw)[2][W], uint32_t (&vw)[2][W], int c, int64_t page) {
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      const int key = base + 8 * i + ks;
-#pragma unroll
-      for (int u = 0; u < W; ++u) {
-        kw[i][u] = 0;
-        vw[i][u] = 0;
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int key = it.kv_begin + CHUNK * c + 8 * i + ks;
       if (key < kv_end) {
-        const int64_t page = page_table[it.page_off + (key >> 4)];
         const int64_t off = (page * 16 + (key & 15)) * slot_stride + head_off;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -539,12 +544,20 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
           kw[i][4 * u] = a.x; kw[i][4 * u + 1] = a.y; kw[i][4 * u + 2] = a.z; kw[i][4 * u + 3] = a.w;
           vw[i][4 * u] = b.x; vw[i][4 * u + 1] = b.y; vw[i][4 * u + 2] = b.z; vw[i][4 * u + 3] = b.w;
         }
+      } else {
+#pragma unroll
+        for (int u = 0; u < W; ++u) {
+          kw[i][u] = 0;
+          vw[i][u] = 0;
+        }
       }
     }
-    float s[STEPS][G];
+  };
+  auto compute = [&](const uint32_t (&kw)[2][W], const uint32_t (&vw)[2][W], int c) {
+    float s[2][G];
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      const bool live = base + 8 * i + ks < kv_end;
+    for (int i = 0; i < 2; ++i) {
+      const bool live = it.kv_begin + CHUNK * c + 8 * i + ks < kv_end;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float acc = 0.0f;
@@ -557,37 +570,61 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
         s[i][j] = live ? acc * scale_log2 : kNegInf;
       }
     }
+    bool any_raise = false;
+    float alpha[G];
+    uint32_t pp[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float mt = s[0][j];
-#pragma unroll
-      for (int i = 1; i < STEPS; ++i) mt = fmaxf(mt, s[i][j]);
-      const float m_new = fmaxf(m[j], mt);
-      const float alpha = (m_new == m[j]) ? 1.0f : fast_exp2(m[j] - m_new);
+      const float mt = fmaxf(s[0][j], s[1][j]);
+      const bool raise = mt > m[j] + kLazyMax;
+      const float m_new = raise ? mt : m[j];
+      alpha[j] = raise ? fast_exp2(m[j] - m_new) : 1.0f;
+      any_raise |= raise;
       const float msub = (m_new == kNegInf) ? 0.0f : m_new;
-      float p[STEPS];
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < STEPS; ++i) {
-        p[i] = fast_exp2(s[i][j] - msub);
-        psum += p[i];
-      }
-      l[j] = l[j] * alpha + psum;
+      const float p0 = fast_exp2(s[0][j] - msub);
+      const float p1 = fast_exp2(s[1][j] - msub);
+      l[j] = l[j] * alpha[j] + p0;
+      l[j] = l[j] + p1;
       m[j] = m_new;
+      pp[j] = pack_bf16x2(p0, p1);
+    }
+    if (__any(any_raise)) {  // lanes whose heads did not raise have alpha == 1
 #pragma unroll
-      for (int u = 0; u < W; ++u) {
-        float a0 = o[j][2 * u] * alpha;
-        float a1 = o[j][2 * u + 1] * alpha;
+      for (int j = 0; j < G; ++j) {
 #pragma unroll
-        for (int i = 0; i < STEPS; ++i) {
-          const uint32_t w = vw[i][u];
-          a0 = __builtin_fmaf(p[i], __builtin_bit_cast(float, w << 16), a0);
-          a1 = __builtin_fmaf(p[i], __builtin_bit_cast(float, w & 0xffff0000u), a1);
-        }
-        o[j][2 * u] = a0;
-        o[j][2 * u + 1] = a1;
+        for (int i = 0; i < DPL; ++i) o[j][i] *= alpha[j];
       }
     }
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const uint32_t v_even = __builtin_amdgcn_perm(vw[1][u], vw[0][u], 0x05040100u);
+      const uint32_t v_odd = __builtin_amdgcn_perm(vw[1][u], vw[0][u], 0x07060302u);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        o[j][2 * u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[j]),
+                                                      __builtin_bit_cast(bf16x2_t, v_even),
+                                                      o[j][2 * u], false);
+        o[j][2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[j]),
+                                                          __builtin_bit_cast(bf16x2_t, v_odd),
+                                                          o[j][2 * u + 1], false);
+      }
+    }
+  };
+
+  // This wave's chunks are wave, wave + 4, ...: two register buffers
+  // alternate; page ids run one chunk ahead of the loads that use them.
+  uint32_t ka[2][W], va[2][W], kb2[2][W], vb2[2][W];
+  int c = wave;
+  if (c < n_chunks) load(ka, va, c, page_of(c));
+  int32_t page_next = page_of(c + 4);
+  for (; c < n_chunks; c += 8) {
+    if (c + 4 < n_chunks) load(kb2, vb2, c + 4, page_next);
+    page_next = page_of(c + 8);
+    compute(ka, va, c);
+    if (c + 4 >= n_chunks) break;
+    if (c + 8 < n_chunks) load(ka, va, c + 8, page_next);
+    page_next = page_of(c + 12);
+    compute(kb2, vb2, c + 4);
   }
 
   // ---- combine the 8 key groups of the wave (butterfly over lane ^ 8, 16, 32) ----
