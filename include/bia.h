@@ -82,6 +82,12 @@ typedef enum bia_mode {
 #define BIA_KV_TILE 64
 #define BIA_PAGE_SIZE 16
 
+/* Plan flags. BIA_PLAN_STRICT_CHUNK_ALIGN: reject (BIA_ERR_INVALID_ARG) a
+ * prefill request whose chunk does not start on the q-tile grid, i.e. whose
+ * kv_len - qo_len is not a multiple of bia_prefill_chunk_align() tokens (the
+ * startup rejection of a misaligned chunk size, sglang PR #43612, Summary). */
+#define BIA_PLAN_STRICT_CHUNK_ALIGN 0x1u
+
 typedef struct bia_plan bia_plan; /* opaque, library-owned */
 
 /*
@@ -100,6 +106,7 @@ typedef struct bia_plan bia_plan; /* opaque, library-owned */
  *       BIA_DECODE_SPLIT for the pages' setting). Keys of request r are cut
  *       into partitions [k * split_size, (k + 1) * split_size), anchored at
  *       key 0 of the request.
+ *   flags: 0 or BIA_PLAN_STRICT_CHUNK_ALIGN.
  * On success *out_plan receives a plan to free with bia_plan_destroy. The
  * arrays are not retained. batch == 0 gives an empty plan whose runs do
  * nothing.
@@ -109,7 +116,8 @@ bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
                            int32_t batch, int32_t num_qo_heads,
                            int32_t num_kv_heads, int32_t head_dim,
                            int32_t page_size, int32_t num_pages,
-                           int32_t split_size, bia_plan** out_plan);
+                           int32_t split_size, uint32_t flags,
+                           bia_plan** out_plan);
 
 /* Bytes of device workspace a run of this plan needs (0 for NULL). */
 size_t bia_plan_workspace_bytes(const bia_plan* plan);
@@ -168,6 +176,24 @@ bia_status bia_merge_states(const float* v, const float* s,
                             const int32_t* state_indptr_dev, int32_t n_rows,
                             int32_t num_heads, int32_t head_dim, void* out,
                             float* out_lse, void* stream);
+
+/*
+ * Write the keys and values of each request's qo_len new tokens into its
+ * pages, before the attention call that reads them (the step ahead of a
+ * chunked prefill or a decode over cached prefix pages, sglang PR #43612,
+ * Summary). New token i of request r is KV position kv_len_r - qo_len_r + i,
+ * slot (position % 16) of page page_table[page_off_r + position / 16].
+ *   k_new, v_new: device bf16 [sum qo_len][Hkv][D], requests packed in order;
+ *   k_pool, v_pool: device bf16 [num_pages][16][Hkv][D], written;
+ *   page_table_dev, workspace: as for bia_prefill_paged (any plan mode).
+ * Only the new tokens' slots are written; every other byte of the pools is
+ * left as it was. Pages shared by two requests of one plan must not receive
+ * new tokens of both (the writes would race).
+ */
+bia_status bia_append_paged_kv(const bia_plan* plan, const void* k_new,
+                               const void* v_new, const int32_t* page_table_dev,
+                               void* k_pool, void* v_pool, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Chunk alignment, in tokens, under which a chunked prefill reproduces the
  * unchunked one bit for bit: 128 (the PREFILL_Q_TILE_TOKENS = 128 constant of

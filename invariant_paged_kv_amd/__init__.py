@@ -19,8 +19,9 @@ Typical use::
 from __future__ import annotations
 
 from ._lib import (BIA_DECODE_SPLIT, BIA_KV_TILE, BIA_MODE_DECODE,
-                   BIA_MODE_PREFILL, BIA_PAGE_SIZE, BIA_PREFILL_SPLIT,
-                   BIA_Q_TILE_ROWS, BiaError, Plan, bia_decode_paged,
+                   BIA_MODE_PREFILL, BIA_PAGE_SIZE, BIA_PLAN_STRICT_CHUNK_ALIGN,
+                   BIA_PREFILL_SPLIT, BIA_Q_TILE_ROWS, BiaError, Plan,
+                   bia_append_paged_kv, bia_decode_paged,
                    bia_last_error, bia_merge_states, bia_plan_create,
                    bia_plan_destroy, bia_plan_workspace_bytes,
                    bia_prefill_chunk_align, bia_prefill_paged, lib_path,
@@ -28,8 +29,8 @@ from ._lib import (BIA_DECODE_SPLIT, BIA_KV_TILE, BIA_MODE_DECODE,
 
 __all__ = [
     "BIA_DECODE_SPLIT", "BIA_KV_TILE", "BIA_MODE_DECODE", "BIA_MODE_PREFILL",
-    "BIA_PAGE_SIZE", "BIA_PREFILL_SPLIT", "BIA_Q_TILE_ROWS", "BiaError", "Plan",
-    "bia_decode_paged", "bia_last_error", "bia_merge_states", "bia_plan_create",
+    "BIA_PAGE_SIZE", "BIA_PLAN_STRICT_CHUNK_ALIGN", "BIA_PREFILL_SPLIT", "BIA_Q_TILE_ROWS",
+    "BiaError", "Plan", "bia_append_paged_kv", "bia_decode_paged", "bia_last_error", "bia_merge_states", "bia_plan_create",
     "bia_plan_destroy", "bia_plan_workspace_bytes", "bia_prefill_chunk_align",
     "bia_prefill_paged", "lib_path", "load_library",
 ]

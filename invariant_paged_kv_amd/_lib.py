@@ -23,6 +23,7 @@ BIA_DECODE_SPLIT = 2048
 BIA_Q_TILE_ROWS = 128
 BIA_KV_TILE = 64
 BIA_PAGE_SIZE = 16
+BIA_PLAN_STRICT_CHUNK_ALIGN = 0x1
 
 _STATUS = {0: "BIA_OK", 1: "BIA_ERR_INVALID_ARG", 2: "BIA_ERR_SHAPE",
            3: "BIA_ERR_PAGE_RANGE", 4: "BIA_ERR_WORKSPACE", 5: "BIA_ERR_UNSUPPORTED",
@@ -58,7 +59,7 @@ def load_library():
     p_i32 = ctypes.POINTER(ctypes.c_int32)
     lib.bia_plan_create.restype = i32
     lib.bia_plan_create.argtypes = [i32, p_i32, p_i32, p_i32, i32, i32, i32, i32, i32,
-                                    i32, i32, ctypes.POINTER(vp)]
+                                    i32, i32, ctypes.c_uint32, ctypes.POINTER(vp)]
     lib.bia_plan_workspace_bytes.restype = sz
     lib.bia_plan_workspace_bytes.argtypes = [vp]
     lib.bia_plan_destroy.restype = None
@@ -68,6 +69,8 @@ def load_library():
     lib.bia_prefill_paged.argtypes = run_args
     lib.bia_decode_paged.restype = i32
     lib.bia_decode_paged.argtypes = run_args
+    lib.bia_append_paged_kv.restype = i32
+    lib.bia_append_paged_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.bia_merge_states.restype = i32
     lib.bia_merge_states.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.bia_prefill_chunk_align.restype = i32
@@ -157,7 +160,7 @@ class Plan:
 
 def bia_plan_create(mode, qo_indptr, kv_indptr, page_table, *, num_qo_heads,
                     num_kv_heads, head_dim, num_pages, split_size,
-                    page_size: int = BIA_PAGE_SIZE) -> Plan:
+                    page_size: int = BIA_PAGE_SIZE, flags: int = 0) -> Plan:
     lib = load_library()
     qo = _host_i32(qo_indptr)
     kv = _host_i32(kv_indptr)
@@ -169,7 +172,7 @@ def bia_plan_create(mode, qo_indptr, kv_indptr, page_table, *, num_qo_heads,
     _check(lib.bia_plan_create(int(mode), _ptr_i32(qo), _ptr_i32(kv),
                                _ptr_i32(pt) if pt.size else None, batch,
                                num_qo_heads, num_kv_heads, head_dim, page_size,
-                               num_pages, split_size, ctypes.byref(handle)))
+                               num_pages, split_size, int(flags), ctypes.byref(handle)))
     kv_lens = np.diff(kv.astype(np.int64))
     total_pages = int(((kv_lens + page_size - 1) // page_size).sum()) if batch else 0
     return Plan(handle.value, int(mode), batch, num_qo_heads, num_kv_heads, head_dim,
@@ -256,6 +259,29 @@ def bia_decode_paged(plan: Plan, q, k_pool, v_pool, page_table_dev, sm_scale, ou
     """Paged decode, one query token per request (see ``bia_decode_paged``)."""
     _run(load_library().bia_decode_paged, plan, BIA_MODE_DECODE, q, k_pool, v_pool,
          page_table_dev, sm_scale, out, lse, workspace, stream)
+
+
+def bia_append_paged_kv(plan: Plan, k_new, v_new, page_table_dev, k_pool, v_pool,
+                        workspace, stream=None):
+    """Write each request's new tokens' K and V into their page slots (see
+    ``bia_append_paged_kv`` in bia.h). ``k_new``/``v_new`` are bf16
+    ``[sum qo_len, Hkv, D]``; the pools are written in place."""
+    torch = _torch()
+    dev = k_new.device if isinstance(k_new, torch.Tensor) else None
+    bf16 = torch.bfloat16
+    Hkv, D = plan.num_kv_heads, plan.head_dim
+    kn = _dev_ptr(k_new, "k_new", bf16, (plan.total_q, Hkv, D))
+    vn = _dev_ptr(v_new, "v_new", bf16, (plan.total_q, Hkv, D), device=dev)
+    pool_shape = (plan.num_pages, BIA_PAGE_SIZE, Hkv, D)
+    kp = _dev_ptr(k_pool, "k_pool", bf16, pool_shape, device=dev)
+    vp = _dev_ptr(v_pool, "v_pool", bf16, pool_shape, device=dev)
+    ptp = _dev_ptr(page_table_dev, "page_table_dev", torch.int32,
+                   min_numel=plan.total_pages, device=dev)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, min_numel=plan.workspace_bytes,
+                  device=dev)
+    _check(load_library().bia_append_paged_kv(ctypes.c_void_p(plan.handle), kn, vn, ptp, kp,
+                                              vp, wp, workspace.numel(),
+                                              _stream_handle(stream, k_new.device)))
 
 
 def bia_merge_states(v, s, state_indptr_dev, out, out_lse=None, stream=None):

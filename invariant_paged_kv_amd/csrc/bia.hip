@@ -110,16 +110,22 @@ __device__ __forceinline__ float fold_finish(float M, float sum, float (&acc)[N]
 // softmax is per lane (plus one exchange with lane ^ 32); then O^T += V^T P^T
 // with the probabilities straight from registers as the B operand.
 //
-// Software pipeline (per wave): the score MFMAs of tile j+1 are issued in the
-// same block as the softmax of tile j, so matrix and vector work overlap;
-// K runs one tile ahead of V through single LDS buffers, refilled from
-// registers loaded two tiles ahead from HBM (two barriers per tile).
+// K and V reach LDS by DMA (global_load_lds_dwordx4: 16 bytes per lane from
+// the lane's own global address into LDS at M0 + 16 * lane, checked on the
+// GPU with an in-bounds probe), so no registers stage them. Two buffers each
+// for K and V; per tile: wait for this wave's DMAs, one barrier, then issue
+// the DMAs of K(j+2) and V(j+1) into the buffers the previous tile finished
+// with, then the score MFMAs of tile j+1 overlapped with the softmax of tile
+// j, then PV of tile j. The DMAs are inline asm with an explicit wait, so the
+// compiler does not make every later LDS read wait for all outstanding loads.
 //
-// LDS: K and V both row-major, [64][D + 8] and [64][D + 16]. K rows are read
-// 16 bytes per lane (the pad keeps 8 consecutive rows on distinct banks); the
-// V^T operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane i
-// addresses 4 dims of key i / 4, and lane j = 4a + b receives dim 4a + b of
-// those 4 keys (the 32-byte pad keeps the 4 rows on distinct banks).
+// LDS rows are 2D bytes, unpadded (a DMA instruction fills 1 KB
+// contiguously); the 16-byte slot of chunk c of row r is c ^ swz(r), which
+// keeps 16 consecutive rows of one chunk (the K operand reads) and 4
+// consecutive rows of 2 chunks (the transposing V reads) on distinct banks.
+// The V^T operand comes from ds_read_b64_tr_b16: in each 16-lane group, lane
+// i addresses 4 dims of key i / 4 and lane j = 4a + b receives dim 4a + b of
+// those 4 keys.
 //
 // MFMA 32x32x16 layouts (lane l, hi = l / 32, c = l % 32): A[m][k]: m = c,
 // k = 8 hi + e; B[k][n]: n = c, k = 8 hi + e; D[m][n]: n = c,
@@ -141,12 +147,30 @@ constexpr float kLazyMax = 8.0f;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
   // p points into __shared__ memory; the C-style cast moves it to the LDS
   // address space, which the transposing read requires.
   const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
   return __builtin_bit_cast(uint2, r);
 }
+
+// Byte offset of a __shared__ address within the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// 16 bytes from this lane's global address to LDS byte lds_base + 16 * lane;
+// lds_base must be the same on every lane of the wave.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(base)
+               : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // max over lanes l and l ^ 32
 __device__ __forceinline__ float max_halves(float x) {
@@ -154,6 +178,16 @@ __device__ __forceinline__ float max_halves(float x) {
                                                   __builtin_bit_cast(unsigned, x), false, false);
   return fmaxf(x, fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])),
                         __builtin_bit_cast(float, static_cast<unsigned>(r[1]))));
+}
+
+// Slot permutation of a row (a bijection on the row's 16-byte slots).
+// D = 128 (16 slots): 16 consecutive rows at one chunk take 16 distinct
+// slots (the K operand reads), and rows 4q..4q+3 at chunks 4b..4b+3 take 16
+// distinct slots (a transposing V read by 32 lanes).
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
 #ifndef BIA_PREFILL_MIN_BLOCKS
@@ -168,18 +202,18 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
                int num_qo_heads, int num_kv_heads, int group_shift, int split,
                uint16_t* __restrict__ out, float* __restrict__ lse_out,
                float* __restrict__ o_part, float* __restrict__ lse_part) {
-  constexpr int KS = D + 8;   // bf16 per K row in LDS
-  constexpr int VS = D + 16;  // bf16 per V row in LDS
-  constexpr int C = D / 8;    // 16-byte chunks per K/V row
-  constexpr int NK = C / 4;   // consecutive keys one thread stages (4 or 2)
-  constexpr int DB = D / 32;  // 32-wide d blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
+  constexpr int RB = D * 2;            // bytes per K/V row in LDS
+  constexpr int SLOTS = D / 8;         // 16-byte slots per row
+  constexpr int RPI = 1024 / RB;       // rows one DMA instruction fills (4 or 8)
+  constexpr int IPW = 64 / (RPI * 4);  // DMA instructions per wave per tile and tensor
+  constexpr int TB = 64 * RB;          // bytes per tile buffer
+  constexpr int DB = D / 32;           // 32-wide d blocks of the output
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TB];  // K0 K1 V0 V1
 
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int hi = lane >> 5;
   const int col = lane & 31;
   const int g = 1 << group_shift;
@@ -205,60 +239,78 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int kv_end = min(it.kv_begin + split, last + 1);
   const int n_tiles = (kv_end - it.kv_begin + 63) >> 6;
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
-
-  // Staging: this thread moves NK consecutive keys (one page: NK divides 16)
-  // times 8 dims of K and V per tile.
-  const int sc = tid % C;
-  const int skey = (tid / C) * NK;
-  const int64_t thread_off = static_cast<int64_t>(it.kv_head) * D + sc * 8;
+  const int64_t head_off = static_cast<int64_t>(it.kv_head) * D;
   const int32_t* pt = page_table + it.page_off;
-  uint4 kreg[NK], vreg[NK];
+  const uint32_t lds_base = lds_offset(lds);
 
-  auto page_of = [&](int t) -> int32_t {
-    const int kk = it.kv_begin + 64 * t + skey;
-    return kk < kv_end ? pt[kk >> 4] : 0;
-  };
-  auto fetch = [&](uint4 (&reg)[NK], const uint16_t* __restrict__ pool, int t,
-                   int64_t page) {
-    const int kk0 = it.kv_begin + 64 * t + skey;
-    const uint16_t* b = pool + (page * 16 + (kk0 & 15)) * slot_stride + thread_off;
-    if (kk0 + NK <= kv_end) {
+  // ---- DMA of one tile of K or V (wave's share: IPW instructions) ----
+  // Instruction r of this wave fills rows row0 .. row0 + RPI - 1 (one page),
+  // row0 = RPI * (4 r + wave); lane l takes row row0 + l / SLOTS and puts its
+  // 16 bytes in slot l % SLOTS, i.e. chunk (l % SLOTS) ^ swz(row).
+  auto pages = [&](int t, int32_t (&pg)[IPW]) {
 #pragma unroll
-      for (int e = 0; e < NK; ++e) reg[e] = *reinterpret_cast<const uint4*>(b + e * slot_stride);
-    } else {  // ragged end of the item: keys at or past kv_end are zero
-#pragma unroll
-      for (int e = 0; e < NK; ++e) {
-        reg[e] = make_uint4(0, 0, 0, 0);
-        if (kk0 + e < kv_end) reg[e] = *reinterpret_cast<const uint4*>(b + e * slot_stride);
-      }
+    for (int r = 0; r < IPW; ++r) {
+      // clamped to the item's last key, so the read is always in range; a
+      // page of a row past kv_end is never used
+      const int k0 = min(it.kv_begin + 64 * t + RPI * (4 * r + wave), kv_end - 1);
+      pg[r] = __builtin_amdgcn_readfirstlane(pt[k0 >> 4]);
     }
   };
-  auto stash_k = [&]() {
+  auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, const int32_t (&pg)[IPW]) {
+    const int t0 = it.kv_begin + 64 * t;
+    auto one = [&](int r, bool guard) {
+      const int row0 = RPI * (4 * r + wave);
+      const int row = row0 + lane / SLOTS;
+      const int chunk = (lane % SLOTS) ^ lds_swz<D>(row);
+      const int key = t0 + row;
+      const int dst = buf * TB + row0 * RB;
+      const uint16_t* src = pool + (static_cast<int64_t>(pg[r]) * 16 + (key & 15)) * slot_stride +
+                            head_off + chunk * 8;
+      if (!guard || key < kv_end) {
+        lds_dma16(src, lds_base + dst);
+      } else {  // past the item's keys: zero, never stale LDS contents
+        *reinterpret_cast<uint4*>(&lds[dst + lane * 16]) = make_uint4(0, 0, 0, 0);
+      }
+    };
+    if (t0 + 64 <= kv_end) {  // uniform: every row of the tile is a key of the item
 #pragma unroll
-    for (int e = 0; e < NK; ++e)
-      *reinterpret_cast<uint4*>(&k_lds[(skey + e) * KS + sc * 8]) = kreg[e];
-  };
-  auto stash_v = [&]() {
+      for (int r = 0; r < IPW; ++r) one(r, false);
+    } else {
 #pragma unroll
-    for (int e = 0; e < NK; ++e)
-      *reinterpret_cast<uint4*>(&v_lds[(skey + e) * VS + sc * 8]) = vreg[e];
+      for (int r = 0; r < IPW; ++r) one(r, true);
+    }
   };
-  auto scores = [&](f32x16 (&acc)[2]) {
+
+  // K operand: row 32 kb + col, chunk 2 s + hi (16 bytes of dims 16 s + 8 hi ..).
+  const int k_sw = lds_swz<D>(col);
+  auto scores = [&](f32x16 (&acc)[2], int buf) {
+    const uint8_t* kb = &lds[buf * TB + col * RB];
     acc[0] = f32x16{};
     acc[1] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
+      const int slot = (2 * s + hi) ^ k_sw;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(
-            &k_lds[(32 * kb + col) * KS + 16 * s + 8 * hi]);
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw), qf[s],
-                                                          acc[kb], 0, 0, 0);
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kb + 32 * kbk * RB + slot * 16);
+        acc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw),
+                                                           qf[s], acc[kbk], 0, 0, 0);
       }
     }
   };
-  // This lane's base in v_lds for the transposed reads (see the header).
-  const int v_lane = (((lane & 15) >> 2) + 4 * hi) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // V^T operand (transposing reads): in 16-lane group G = lane / 16 (hi = G / 2,
+  // dims 16 (G % 2) ..), lane i = lane % 16 addresses key kq = i / 4 of the
+  // 4-key run and dims 4 (i % 4) .. + 3; the second read of an MFMA is 8 keys on.
+  const int vq = (lane & 15) >> 2;
+  const int v_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 32-dim block
+  const int v_byte = (lane & 1) * 8;
+  int v_row_off[2], v_sw[2];
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    const int r = 4 * hi + 8 * e2 + vq;  // row modulo 16 (32 kb + 16 h do not change swz)
+    v_row_off[e2] = r * RB + v_byte;
+    v_sw[e2] = lds_swz<D>(r);
+  }
 
   float m = kNegInf;  // running max (base-2 scaled logits), possibly stale by < kLazyMax
   float lsum = 0.0f;  // this lane-half's running sum of probabilities
@@ -266,71 +318,124 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x16{};
 
-  // ---- prologue: K(0), V(0) in LDS; S = scores of tile 0; K(1) in LDS;
-  // registers hold K(2) and V(1); page ids for V(2) and K(3) ready ----
+  // ---- prologue: K(0), V(0), K(1) by DMA; scores of tile 0 ----
   f32x16 sacc[2];
-  {
-    const int32_t p0 = page_of(0);
-    const int32_t p1 = page_of(1);
-    const int32_t p2 = page_of(2);
-    fetch(kreg, kp, 0, p0);
-    fetch(vreg, vp, 0, p0);
-    stash_k();
-    stash_v();
-    if (n_tiles > 1) {
-      fetch(kreg, kp, 1, p1);
-      fetch(vreg, vp, 1, p1);
-    }
-    __syncthreads();
-    scores(sacc);
-    __syncthreads();
-    if (n_tiles > 1) stash_k();
-    if (n_tiles > 2) fetch(kreg, kp, 2, p2);
-    __syncthreads();
-  }
-  int32_t page_v = page_of(2);  // page ids for V(j + 2) and K(j + 3)
-  int32_t page_k = page_of(3);
+  int32_t pg_v[IPW], pg_k[IPW];
+  pages(0, pg_v);
+  issue(kp, 0, 0, pg_v);
+  issue(vp, 0, 2, pg_v);
+  pages(1, pg_v);
+  if (n_tiles > 1) issue(kp, 1, 1, pg_v);
+  pages(2, pg_k);
+  wait_dma();
+  __syncthreads();
+  scores(sacc, 0);
 
-  // One tile of the pipeline: softmax of `cur` (tile j) overlapped with the
-  // score MFMAs of tile j+1 into `nxt` (when HasNext), then PV of tile j and
-  // the LDS/register refills for the tiles after it.
-  auto body = [&](auto has_next, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) {
+  // One tile: wait + barrier, DMAs of K(j+2) and V(j+1), score MFMAs of tile
+  // j+1 (into nxt) overlapped with the softmax of tile j (cur), PV of tile j.
+  // P is the parity of j (K(j+1) is in buffer 1 - P, V(j) in buffer 2 + P).
+  // K fragment of score MFMA i (head-dim step i / 2, key block i % 2).
+  auto kfrag = [&](int buf, int i) -> bf16x8 {
+    const int slot = (2 * (i >> 1) + hi) ^ k_sw;
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(&lds[buf * TB + (32 * (i & 1) + col) * RB +
+                                                     slot * 16]));
+  };
+  // V^T fragment of PV MFMA i: key block kb = i / (2 DB), half h = (i / DB) % 2,
+  // dim block b = i % DB (so consecutive MFMAs accumulate into different o[b]).
+  auto vfrag = [&](int buf, int i) -> bf16x8 {
+    const int b = i % DB;
+    const int kbk = i / (2 * DB);
+    const int h = (i / DB) & 1;
+    const uint8_t* rb = &lds[buf * TB + (32 * kbk + 16 * h) * RB];
+    const uint2 lo = lds_read_tr16(rb + v_row_off[0] + ((4 * b + v_lo) ^ v_sw[0]) * 16);
+    const uint2 up = lds_read_tr16(rb + v_row_off[1] + ((4 * b + v_lo) ^ v_sw[1]) * 16);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, up.x, up.y));
+  };
+
+  // One tile: wait + barrier; DMAs of K(j+2) and V(j+1) into the buffers the
+  // previous tile finished with; phase A: the 16 score MFMAs of tile j+1 (into
+  // nxt) hand-interleaved with the softmax of tile j (cur), K reads two MFMAs
+  // ahead; phase B: the PV MFMAs of tile j, V reads two MFMAs ahead. Each
+  // group ends in a scheduling fence so the compiler keeps the interleave.
+  // P is the parity of j (K(j+1) is in buffer 1 - P, V(j) in buffer 2 + P).
+  auto body = [&](auto has_next, auto parity, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) {
     constexpr bool kHasNext = decltype(has_next)::value;
+    constexpr int P = decltype(parity)::value;
+    wait_dma();
+    __syncthreads();  // K(j+1), V(j) are in LDS; every wave is done with tile j-1
+    if constexpr (kHasNext) {
+      if (j + 2 < n_tiles) issue(kp, j + 2, P, pg_k);
+      issue(vp, j + 1, 3 - P, pg_v);
+#pragma unroll
+      for (int r = 0; r < IPW; ++r) pg_v[r] = pg_k[r];
+      pages(j + 3, pg_k);
+    }
     const int t0 = it.kv_begin + 64 * j;
     if (t0 + 63 > wave_pos0) {  // wave-uniform: some key is past some row
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = t0 + 32 * kb + 8 * (v >> 2) + 4 * hi + (v & 3);
-          cur[kb][v] = key <= pos ? cur[kb][v] : kNegInf;
+          const int key = t0 + 32 * kbk + 8 * (v >> 2) + 4 * hi + (v & 3);
+          cur[kbk][v] = key <= pos ? cur[kbk][v] : kNegInf;
         }
       }
     }
-    if constexpr (kHasNext) scores(nxt);
-    float mt = kNegInf;
+
+    // ---- phase A ----
+    float mq[4];
+    float m_new = m, alpha = 1.0f, neg_m = 0.0f, psum = 0.0f;
+    bool raise = false;
+    uint32_t pw[16];  // packed bf16 probabilities, pair pi = 8 kb + (v / 2)
+    auto softmax_step = [&](int i) {
+      if (i < 4) {
+        const int kbk = i >> 1, v0 = 8 * (i & 1);
+        float x = cur[kbk][v0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int v = 1; v < 8; ++v) x = fmaxf(x, cur[kbk][v0 + v]);
+        mq[i] = x;
+      } else if (i == 4) {
+        const float mt = max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * scale_log2;
+        raise = mt > m + kLazyMax;  // true on the first tile with a visible key
+        m_new = raise ? mt : m;
+        alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+        neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+      } else if (i < 13) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, cur[kb][v]);
-    }
-    mt = max_halves(mt) * scale_log2;
-    const bool raise = mt > m + kLazyMax;  // true on the first tile with a visible key
-    const float m_new = raise ? mt : m;
-    const float alpha = raise ? fast_exp2(m - m_new) : 1.0f;
-    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-    float psum = 0.0f;
-    uint32_t pw[2][2][4];  // [kb][half][pair] packed bf16 probabilities
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(cur[kb][v], scale_log2, neg_m));
-        const float p1 = fast_exp2(__builtin_fmaf(cur[kb][v + 1], scale_log2, neg_m));
-        psum += p0;
-        psum += p1;
-        pw[kb][v >> 3][(v & 7) >> 1] = pack_bf16x2(p0, p1);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int pi = 2 * (i - 5) + q2;
+          const int kbk = pi >> 3, v = 2 * (pi & 7);
+          const float p0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m));
+          psum += p0;
+          psum += p1;
+          pw[pi] = pack_bf16x2(p0, p1);
+          // keep this step's results here: without it the compiler sinks
+          // them past the rescale branch, out of the interleave
+          asm volatile("" : "+v"(pw[pi]), "+v"(psum));
+        }
       }
+    };
+    if constexpr (kHasNext) {
+      nxt[0] = f32x16{};
+      nxt[1] = f32x16{};
+      bf16x8 kf[3];
+      kf[0] = kfrag(1 - P, 0);
+      kf[1] = kfrag(1 - P, 1);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[i >> 1], nxt[i & 1],
+                                                             0, 0, 0);
+        if (i + 2 < D / 8) kf[(i + 2) % 3] = kfrag(1 - P, i + 2);
+        if (i < 16) softmax_step(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = D / 8; i < 16; ++i) softmax_step(i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) softmax_step(i);
     }
     if (__any(raise)) {  // lanes that did not raise have alpha == 1 exactly
       lsum *= alpha;
@@ -340,54 +445,40 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     lsum += psum;
     m = m_new;
 
-    // Every wave is done reading K(j+1), and V(j), stored by all waves after
-    // the previous tile's second barrier, is visible. The last tile needs the
-    // barrier for the second reason alone.
-    __syncthreads();
-    if constexpr (kHasNext) {
-      if (j + 2 < n_tiles) stash_k();
-      if (j + 3 < n_tiles) fetch(kreg, kp, j + 3, page_k);
-    }
-
-    // ---- O^T += V^T P^T (V of tile j) ----
+    // ---- phase B: O^T += V^T P^T (V of tile j, buffer 2 + P) ----
+    constexpr int NPV = 4 * DB;
+    bf16x8 vf[3];
+    vf[0] = vfrag(2 + P, 0);
+    vf[1] = vfrag(2 + P, 1);
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint16_t* src = &v_lds[v_lane + (32 * kb + 16 * h) * VS + 32 * b];
-          const uint2 lo = lds_read_tr16(src);
-          const uint2 up = lds_read_tr16(src + 8 * VS);
-          const uint4 va = make_uint4(lo.x, lo.y, up.x, up.y);
-          const uint4 pb = make_uint4(pw[kb][h][0], pw[kb][h][1], pw[kb][h][2], pw[kb][h][3]);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), o[b], 0, 0, 0);
-        }
-      }
-    }
-    if constexpr (kHasNext) {
-      __syncthreads();  // every wave is done reading V(j)
-      stash_v();        // V(j+1)
-      if (j + 2 < n_tiles) fetch(vreg, vp, j + 2, page_v);
-      page_v = page_k;
-      page_k = page_of(j + 4);
+    for (int i = 0; i < NPV; ++i) {
+      const int b = i % DB;
+      const int pb0 = 4 * (i / DB);  // first pair of (kb, h)
+      const uint4 pb = make_uint4(pw[pb0], pw[pb0 + 1], pw[pb0 + 2], pw[pb0 + 3]);
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], __builtin_bit_cast(bf16x8, pb),
+                                                     o[b], 0, 0, 0);
+      if (i + 2 < NPV) vf[(i + 2) % 3] = vfrag(2 + P, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Unrolled by two so the score registers alternate without copies; the
-  // last tile has no successor to prefetch.
+  // Unrolled by two so the score registers alternate without copies and the
+  // buffer parity is a constant; the last tile has no successor.
+  using T = std::true_type;
+  using F = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   f32x16 sb[2];
   int j = 0;
   for (; j + 2 < n_tiles; j += 2) {
-    body(std::true_type{}, sacc, sb, j);
-    body(std::true_type{}, sb, sacc, j + 1);
+    body(T{}, P0{}, sacc, sb, j);
+    body(T{}, P1{}, sb, sacc, j + 1);
   }
   if (j + 1 < n_tiles) {
-    body(std::true_type{}, sacc, sb, j);
-    body(std::false_type{}, sb, sacc, j + 1);
+    body(T{}, P0{}, sacc, sb, j);
+    body(F{}, P1{}, sb, sacc, j + 1);
   } else {
-    body(std::false_type{}, sacc, sb, j);
+    body(F{}, P0{}, sacc, sb, j);
   }
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----
@@ -746,6 +837,30 @@ merge_states_kernel(const float* __restrict__ v, const float* __restrict__ s,
 }
 
 // ---------------------------------------------------------------------------
+// KV append: one workgroup per AppendItem copies up to 16 new tokens (all kv
+// heads, K and V) of one request from the packed k_new / v_new rows into
+// their page slots. 16-byte copies; a token's Hkv * D row is contiguous on
+// both sides.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restrict__ k_new,
+              const uint16_t* __restrict__ v_new, const int32_t* __restrict__ page_table,
+              int row_elems, uint16_t* __restrict__ kp, uint16_t* __restrict__ vp) {
+  const bia::AppendItem a = items[blockIdx.x];
+  const int chunks = row_elems / 8;  // 16-byte pieces per token row
+  for (int e = threadIdx.x; e < a.n_tok * chunks; e += kThreads) {
+    const int t = e / chunks;
+    const int c = e % chunks;
+    const int pos = a.dst_pos0 + t;
+    const int64_t page = page_table[a.page_off + (pos >> 4)];
+    const int64_t dst = (page * 16 + (pos & 15)) * row_elems + c * 8;
+    const int64_t src = static_cast<int64_t>(a.src_row0 + t) * row_elems + c * 8;
+    *reinterpret_cast<uint4*>(kp + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(vp + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch layer.
 // ---------------------------------------------------------------------------
 std::mutex g_pin_mutex;
@@ -943,5 +1058,34 @@ extern "C" bia_status bia_merge_states(const float* v, const float* s,
                        out_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return BIA_OK;
+}
+
+extern "C" bia_status bia_append_paged_kv(const bia_plan* plan, const void* k_new,
+                                          const void* v_new, const int32_t* page_table_dev,
+                                          void* k_pool, void* v_pool, void* workspace,
+                                          size_t workspace_bytes, void* stream_handle) {
+  if (plan == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "plan is NULL");
+  const bia::PlanData& d = plan->d;
+  if (d.appends.empty()) return BIA_OK;
+  if (k_new == nullptr || v_new == nullptr || page_table_dev == nullptr || k_pool == nullptr ||
+      v_pool == nullptr)
+    return bia::fail(BIA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (workspace == nullptr || workspace_bytes < d.ws_bytes)
+    return bia::fail(BIA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed",
+                     workspace == nullptr ? size_t(0) : workspace_bytes, d.ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % bia::kWsAlign != 0)
+    return bia::fail(BIA_ERR_WORKSPACE, "workspace is not %zu-byte aligned", bia::kWsAlign);
+  hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+  bia_status st = upload(plan, workspace, stream);
+  if (st != BIA_OK) return st;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(d.appends.size())), dim3(kThreads),
+                     0, stream, reinterpret_cast<const bia::AppendItem*>(ws + d.off_appends),
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     page_table_dev, d.num_kv_heads * d.head_dim, static_cast<uint16_t*>(k_pool),
+                     static_cast<uint16_t*>(v_pool));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "append launch");
   return BIA_OK;
 }

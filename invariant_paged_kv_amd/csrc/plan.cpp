@@ -61,6 +61,9 @@ static bia_status build(PlanData& d, const int32_t* qo_indptr,
   for (int32_t r = 0; r < d.batch; ++r) {
     const int32_t qo_len = qo_indptr[r + 1] - qo_indptr[r];
     const int32_t kv_len = kv_indptr[r + 1] - kv_indptr[r];
+    for (int32_t t0 = 0; t0 < qo_len; t0 += kAppendTokens)
+      d.appends.push_back(AppendItem{qo_indptr[r] + t0, std::min(kAppendTokens, qo_len - t0),
+                                     kv_len - qo_len + t0, static_cast<int32_t>(page_off)});
     for (int32_t t0 = 0; t0 < qo_len; t0 += T) {
       const int32_t n_tok = std::min(T, qo_len - t0);
       const int32_t pos0 = kv_len - qo_len + t0;
@@ -110,7 +113,7 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
                                       int32_t num_qo_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t page_size,
                                       int32_t num_pages, int32_t split_size,
-                                      bia_plan** out_plan) {
+                                      uint32_t flags, bia_plan** out_plan) {
   if (out_plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out_plan is NULL");
   *out_plan = nullptr;
   if (mode != BIA_MODE_PREFILL && mode != BIA_MODE_DECODE)
@@ -137,6 +140,8 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
                 "split_size %d must be a positive multiple of the %d-key KV tile",
                 split_size, kKvTile);
 
+  if ((flags & ~BIA_PLAN_STRICT_CHUNK_ALIGN) != 0)
+    return fail(BIA_ERR_INVALID_ARG, "unknown plan flags 0x%x", flags);
   int64_t total_pages = 0;
   if (batch > 0) {
     if (qo_indptr[0] != 0 || kv_indptr[0] != 0)
@@ -152,6 +157,11 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
       if (mode == BIA_MODE_DECODE && qo != 1)
         return fail(BIA_ERR_SHAPE, "request %d: decode needs qo_len 1, got %lld", r,
                     static_cast<long long>(qo));
+      if (mode == BIA_MODE_PREFILL && (flags & BIA_PLAN_STRICT_CHUNK_ALIGN) && qo > 0 &&
+          (kv - qo) % kQTileRows != 0)
+        return fail(BIA_ERR_INVALID_ARG,
+                    "request %d: chunk starts at token %lld, not aligned to %d tokens", r,
+                    static_cast<long long>(kv - qo), kQTileRows);
       total_pages += ceil_div(kv, page_size);
     }
     if (total_pages > 0 && page_table == nullptr)
@@ -176,6 +186,7 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   d.page_size = page_size;
   d.num_pages = num_pages;
   d.split = split_size;
+  d.flags = flags;
   d.group = group;
   d.tile_tokens = kQTileRows / group;
   d.total_q = batch > 0 ? qo_indptr[batch] : 0;
@@ -192,7 +203,8 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   }
   d.off_items = 0;
   d.off_merges = d.items.size() * sizeof(WorkItem);
-  d.blob_bytes = d.off_merges + d.merges.size() * sizeof(MergeItem);
+  d.off_appends = d.off_merges + d.merges.size() * sizeof(MergeItem);
+  d.blob_bytes = d.off_appends + d.appends.size() * sizeof(AppendItem);
   d.off_o = align_up(d.blob_bytes, kWsAlign);
   d.off_lse = align_up(d.off_o + size_t(d.n_states) * head_dim * sizeof(float), kWsAlign);
   d.ws_bytes = d.n_states > 0 ? d.off_lse + size_t(d.n_states) * sizeof(float)
@@ -204,6 +216,9 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   if (!d.merges.empty())
     std::memcpy(d.blob.data() + d.off_merges, d.merges.data(),
                 d.merges.size() * sizeof(MergeItem));
+  if (!d.appends.empty())
+    std::memcpy(d.blob.data() + d.off_appends, d.appends.data(),
+                d.appends.size() * sizeof(AppendItem));
   *out_plan = plan;
   return BIA_OK;
 }

@@ -34,7 +34,16 @@ struct MergeItem {
   int32_t state0, n_splits, q_row0, n_tok, kv_head, stride, pad0, pad1;
 };
 
+// Copy of up to kAppendTokens new tokens of one request into its pages:
+// rows src_row0 .. src_row0 + n_tok - 1 of k_new / v_new go to KV positions
+// dst_pos0 .. ; the request's pages start at page_table[page_off].
+struct AppendItem {
+  int32_t src_row0, n_tok, dst_pos0, page_off;
+};
+constexpr int kAppendTokens = 16;
+
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
+static_assert(sizeof(AppendItem) == 16, "append item is 4 int32");
 static_assert(sizeof(MergeItem) == 32, "merge item is 8 int32");
 
 constexpr int kQTileRows = BIA_Q_TILE_ROWS;
@@ -46,14 +55,17 @@ struct PlanData {
   bia_mode mode;
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages;
   int32_t split, group, tile_tokens;
+  uint32_t flags;
   int64_t total_q;   // sum of qo_len: rows of q / out
   int64_t n_states;  // partial states written before the merge
   std::vector<WorkItem> items;
   std::vector<MergeItem> merges;
-  // Workspace layout (byte offsets): [items | merges] (the uploaded blob),
-  // then fp32 o[n_states][head_dim], then fp32 lse[n_states].
-  size_t off_items, off_merges, off_o, off_lse, blob_bytes, ws_bytes;
-  std::vector<unsigned char> blob;  // host copy of [items | merges]
+  std::vector<AppendItem> appends;
+  // Workspace layout (byte offsets): [items | merges | appends] (the
+  // uploaded blob), then fp32 o[n_states][head_dim], then fp32
+  // lse[n_states].
+  size_t off_items, off_merges, off_appends, off_o, off_lse, blob_bytes, ws_bytes;
+  std::vector<unsigned char> blob;  // host copy of [items | merges | appends]
 };
 
 void set_error(const char* fmt, ...);

@@ -46,12 +46,12 @@ def test_chunk_align_is_128():
 
 def plan(mode=bia.BIA_MODE_PREFILL, qo=(0, 100, 400), kv=(0, 100, 400), pt=None,
          heads=dict(num_qo_heads=4, num_kv_heads=1, head_dim=64), num_pages=64,
-         split=4096):
+         split=4096, flags=0):
     if pt is None:
         kvl = np.diff(kv)
         pt = np.arange(int(((kvl + 15) // 16).sum()))
     return bia.bia_plan_create(mode, qo, kv, pt, num_pages=num_pages, split_size=split,
-                               **heads)
+                               flags=flags, **heads)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -68,6 +68,13 @@ def plan(mode=bia.BIA_MODE_PREFILL, qo=(0, 100, 400), kv=(0, 100, 400), pt=None,
     (dict(heads=dict(num_qo_heads=48, num_kv_heads=3, head_dim=64)), "BIA_ERR_UNSUPPORTED"),
     (dict(mode=bia.BIA_MODE_DECODE), "BIA_ERR_SHAPE"),            # decode needs qo_len 1
     (dict(mode=7), "BIA_ERR_INVALID_ARG"),
+    (dict(flags=0x2), "BIA_ERR_INVALID_ARG"),                     # unknown flag
+    # strict chunk alignment: starts at 0 and 128 pass, 100 is rejected
+    (dict(qo=(0, 100, 400), kv=(0, 100, 400), flags=1), None),
+    (dict(qo=(0, 172), kv=(0, 300), flags=1), None),
+    (dict(qo=(0, 200), kv=(0, 300), flags=1), "BIA_ERR_INVALID_ARG"),
+    (dict(qo=(0, 200), kv=(0, 300), flags=0), None),
+    (dict(mode=bia.BIA_MODE_DECODE, qo=(0, 1), kv=(0, 300), flags=1), None),
 ])
 def test_plan_validation(kwargs, status):
     if status is None:
@@ -77,15 +84,18 @@ def test_plan_validation(kwargs, status):
         plan(**kwargs)
     assert str(e.value).startswith(status), str(e.value)
     assert bia.bia_last_error()
+    if kwargs.get("flags") == 1:
+        assert "aligned to 128 tokens" in bia.bia_last_error()
 
 
 def test_null_pointers_rejected_before_anything_runs():
     lib = bia.load_library()
     h = ctypes.c_void_p()
-    assert lib.bia_plan_create(0, None, None, None, 2, 4, 1, 64, 16, 64, 4096,
+    assert lib.bia_plan_create(0, None, None, None, 2, 4, 1, 64, 16, 64, 4096, 0,
                                ctypes.byref(h)) == 1
-    assert lib.bia_plan_create(0, None, None, None, 0, 4, 1, 64, 16, 64, 4096,
+    assert lib.bia_plan_create(0, None, None, None, 0, 4, 1, 64, 16, 64, 4096, 0,
                                None) == 1
+    assert lib.bia_append_paged_kv(None, None, None, None, None, None, None, 0, None) == 1
     # run calls with a NULL plan fail in the argument check (no HIP call)
     assert lib.bia_prefill_paged(None, None, None, None, None, 1.0, None, None, None, 0,
                                  None) == 1
@@ -222,3 +232,14 @@ def test_workspace_grows_with_states():
     assert a.num_states == 0 and b.num_states > 0
     assert b.workspace_bytes >= b.num_states * (128 + 1) * 4
     assert a.workspace_bytes % 256 == 0 and b.workspace_bytes > a.workspace_bytes
+
+
+def test_append_items_in_workspace():
+    """The plan's uploaded blob grows by one 16-byte append item per 16 new
+    tokens of each request."""
+    a = plan(qo=(0, 16), kv=(0, 16))
+    b = plan(qo=(0, 17), kv=(0, 17))
+    c = plan(qo=(0, 0, 1), kv=(0, 20, 21))
+    assert a.workspace_bytes >= 2 * 32 + 16     # 1 tile item (g=4: 32 tokens) + 1 append
+    assert b.workspace_bytes >= 32 + 2 * 16     # 1 tile item + 2 appends
+    assert c.workspace_bytes >= 32 + 16
