@@ -170,6 +170,30 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) 
                : "memory");
 }
 
+__host__ __device__ constexpr uint64_t join_u64(uint32_t hi, uint32_t lo) {
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+static_assert(join_u64(0x00007f12u, 0x80004000u) == 0x00007f1280004000ull,
+              "64-bit address widening must not sign-extend the low word");
+
+// Same, with the global address split into a wave-uniform 64-bit base (an
+// SGPR pair) and this lane's 32-bit byte offset from it.
+__device__ __forceinline__ void lds_dma16_sbase(uint32_t lane_off, const void* base,
+                                                uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // readfirstlane returns int: each half goes through uint32_t, or the low
+  // half would sign-extend into the high word.
+  const uint64_t sb = join_u64(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                                   static_cast<uint32_t>(b >> 32))),
+                               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                                   static_cast<uint32_t>(b))));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(sb), "s"(m0)
+               : "memory");
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // max over lanes l and l ^ 32
@@ -256,28 +280,37 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
       pg[r] = __builtin_amdgcn_readfirstlane(pt[k0 >> 4]);
     }
   };
+  // A lane's rows within a page and its chunk are the same for every DMA
+  // instruction of every tile (row0 is a multiple of 16 apart between
+  // instructions), so its byte offset from the page base is one constant.
+  const int dma_row = RPI * wave + lane / SLOTS;  // row of instruction 0 (mod 16)
+  const uint32_t dma_lane_off = static_cast<uint32_t>(
+      ((dma_row & 15) * slot_stride + head_off + ((lane % SLOTS) ^ lds_swz<D>(dma_row)) * 8) * 2);
   auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, const int32_t (&pg)[IPW]) {
     const int t0 = it.kv_begin + 64 * t;
-    auto one = [&](int r, bool guard) {
-      const int row0 = RPI * (4 * r + wave);
-      const int row = row0 + lane / SLOTS;
-      const int chunk = (lane % SLOTS) ^ lds_swz<D>(row);
-      const int key = t0 + row;
-      const int dst = buf * TB + row0 * RB;
-      const uint16_t* src = pool + (static_cast<int64_t>(pg[r]) * 16 + (key & 15)) * slot_stride +
-                            head_off + chunk * 8;
-      if (!guard || key < kv_end) {
-        lds_dma16(src, lds_base + dst);
-      } else {  // past the item's keys: zero, never stale LDS contents
-        *reinterpret_cast<uint4*>(&lds[dst + lane * 16]) = make_uint4(0, 0, 0, 0);
-      }
-    };
     if (t0 + 64 <= kv_end) {  // uniform: every row of the tile is a key of the item
 #pragma unroll
-      for (int r = 0; r < IPW; ++r) one(r, false);
+      for (int r = 0; r < IPW; ++r) {
+        const int row0 = RPI * (4 * r + wave);
+        const uint16_t* page_base = pool + static_cast<int64_t>(pg[r]) * 16 * slot_stride;
+        lds_dma16_sbase(dma_lane_off, page_base, lds_base + buf * TB + row0 * RB);
+      }
     } else {
 #pragma unroll
-      for (int r = 0; r < IPW; ++r) one(r, true);
+      for (int r = 0; r < IPW; ++r) {
+        const int row0 = RPI * (4 * r + wave);
+        const int row = row0 + lane / SLOTS;
+        const int chunk = (lane % SLOTS) ^ lds_swz<D>(row);
+        const int key = t0 + row;
+        const int dst = buf * TB + row0 * RB;
+        if (key < kv_end) {
+          const uint16_t* src = pool + (static_cast<int64_t>(pg[r]) * 16 + (key & 15)) *
+                                           slot_stride + head_off + chunk * 8;
+          lds_dma16(src, lds_base + dst);
+        } else {  // past the item's keys: zero, never stale LDS contents
+          *reinterpret_cast<uint4*>(&lds[dst + lane * 16]) = make_uint4(0, 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -547,6 +580,27 @@ __device__ __forceinline__ float dpp_sum8(float x) {
   x = x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                         0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
   return x;
+}
+
+// Value of lane ^ 8 (within each 16-lane row).
+__device__ __forceinline__ float dpp_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x128, 0xF, 0xF, false));
+}
+
+// {x of this lane, x of lane ^ 16} (step 0) or {.., lane ^ 32} (step 1), in
+// an order that depends on the lane.
+__device__ __forceinline__ void lane_swap(int step, float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  if (step == 0) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+  }
 }
 
 // Symmetric combine of two base-2 online-softmax states (same result on both
