@@ -773,16 +773,31 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   }
 
   // ---- combine the 8 key groups of the wave (butterfly over lane ^ 8, 16, 32) ----
+  // lane ^ 8: DPP row_ror:8 brings the partner's value. lane ^ 16 and ^ 32:
+  // v_permlane16/32_swap return {own value, partner's value} in an order
+  // that depends on the lane; combine_sym is symmetric, so both lanes of a
+  // pair combine the same two states and get the same bits either way.
 #pragma unroll
-  for (int mask = 8; mask <= 32; mask <<= 1) {
+  for (int j = 0; j < G; ++j) {
+    float o2[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o2[i] = dpp_ror8(o[j][i]);
+    combine_sym<DPL>(m[j], l[j], o[j], dpp_ror8(m[j]), dpp_ror8(l[j]), o2);
+  }
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float o2[DPL];
+      float oa[DPL], ob[DPL], ma, mb, la, lb;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) o2[i] = __shfl_xor(o[j][i], mask);
-      const float m2 = __shfl_xor(m[j], mask);
-      const float l2 = __shfl_xor(l[j], mask);
-      combine_sym<DPL>(m[j], l[j], o[j], m2, l2, o2);
+      for (int i = 0; i < DPL; ++i) lane_swap(step, o[j][i], oa[i], ob[i]);
+      lane_swap(step, m[j], ma, mb);
+      lane_swap(step, l[j], la, lb);
+      combine_sym<DPL>(ma, la, oa, mb, lb, ob);
+      m[j] = ma;
+      l[j] = la;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[j][i] = oa[i];
     }
   }
   if (ks == 0) {
