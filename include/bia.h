@@ -195,6 +195,67 @@ bia_status bia_append_paged_kv(const bia_plan* plan, const void* k_new,
                                void* k_pool, void* v_pool, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Decode without host planning, for callers that replay it from a HIP graph
+ * (a captured call holds no host-to-device copy and allocates nothing). The
+ * pages' runtime turns split-KV off while capturing and replaying graphs
+ * ("[POC] Support deterministic inference", sglang PR #10417, Modifications,
+ * and the review thread on disable_split_kv), so its bits depend on whether
+ * a graph ran; here the partitions stay at split_size in graph mode, and a
+ * request's out / lse bits equal those of bia_decode_paged with a plan of
+ * the same split_size.
+ *
+ * bia_decode_graph_create fixes the capacity: up to max_batch requests, each
+ * with 1 <= kv_len <= max_kv_len, and page tables of up to
+ * page_table_capacity entries. The other arguments are as for
+ * bia_plan_create (head_dim 64 or 128, page_size 16, split_size a positive
+ * multiple of 64). The handle is host memory owned by the library.
+ *
+ * bia_decode_graph_workspace_bytes: bytes of workspace a run needs (it holds
+ * the per-request flags, the work list made on the device and the partial
+ * states of up to ceil(max_kv_len / split_size) partitions per request and
+ * kv head).
+ *
+ * bia_decode_graph_run: decode of `batch` requests (0 <= batch <= max_batch;
+ * `batch` and every pointer are baked into a captured graph, the contents of
+ * the buffers are not). kv_indptr_dev: device int32 [batch + 1], starting at
+ * 0 (cumulative kv lengths, as kv_indptr of bia_plan_create); q, out: device
+ * bf16 [batch][Hq][D]; lse: device fp32 [batch][Hq] or NULL; page_table_dev:
+ * device int32 with request r's pages at page_off_r as for the other calls;
+ * workspace: device, >= bia_decode_graph_workspace_bytes, 256-byte aligned.
+ * Launches a planner kernel (one workgroup per request), the decode kernel
+ * over batch * Hkv * ceil(max_kv_len / split_size) fixed slots (slots past a
+ * request's partitions return at once) and, when a request can span more
+ * than one partition, the fixed-order merge. Host-side checks run before
+ * anything is enqueued; the device checks each request (1 <= kv_len <=
+ * max_kv_len, its pages within page_table_capacity, every page id in
+ * [0, num_pages)) and an invalid request reads no keys: its rows come out as
+ * the empty state (o = 0, lse = -inf) and its flag is set.
+ *
+ * bia_decode_graph_read_flags: copies the flags of the last run on this
+ * workspace to host int32 [batch] and waits for the stream (not for use
+ * inside a captured region): 0 = valid, else a sum of 1 (kv_len outside
+ * [1, max_kv_len]), 2 (pages past page_table_capacity), 4 (a page id outside
+ * [0, num_pages)).
+ */
+typedef struct bia_decode_graph bia_decode_graph; /* opaque, library-owned */
+bia_status bia_decode_graph_create(int32_t max_batch, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, int32_t num_pages,
+                                   int32_t max_kv_len, int32_t page_table_capacity,
+                                   int32_t split_size, bia_decode_graph** out);
+size_t bia_decode_graph_workspace_bytes(const bia_decode_graph* dg);
+void bia_decode_graph_destroy(bia_decode_graph* dg);
+bia_status bia_decode_graph_run(const bia_decode_graph* dg, int32_t batch,
+                                const int32_t* kv_indptr_dev, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* page_table_dev, float sm_scale,
+                                void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+bia_status bia_decode_graph_read_flags(const bia_decode_graph* dg,
+                                       const void* workspace, int32_t batch,
+                                       int32_t* flags_host, void* stream);
+
 /* Chunk alignment, in tokens, under which a chunked prefill reproduces the
  * unchunked one bit for bit: 128 (the PREFILL_Q_TILE_TOKENS = 128 constant of
  * sglang PR #43612, Summary). Chunk starts that are multiples of it land on

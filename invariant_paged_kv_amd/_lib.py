@@ -83,6 +83,17 @@ def load_library():
     lib.bia_plan_get_items.argtypes = [vp, p_i32, i32]
     lib.bia_plan_num_states.restype = i64
     lib.bia_plan_num_states.argtypes = [vp]
+    lib.bia_decode_graph_create.restype = i32
+    lib.bia_decode_graph_create.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(vp)]
+    lib.bia_decode_graph_workspace_bytes.restype = sz
+    lib.bia_decode_graph_workspace_bytes.argtypes = [vp]
+    lib.bia_decode_graph_destroy.restype = None
+    lib.bia_decode_graph_destroy.argtypes = [vp]
+    lib.bia_decode_graph_run.restype = i32
+    lib.bia_decode_graph_run.argtypes = [vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.bia_decode_graph_read_flags.restype = i32
+    lib.bia_decode_graph_read_flags.argtypes = [vp, vp, i32, p_i32, vp]
     _lib = lib
     return lib
 
@@ -306,3 +317,101 @@ def bia_merge_states(v, s, state_indptr_dev, out, out_lse=None, stream=None):
                                               (n_rows, H), device=dev)
     _check(lib.bia_merge_states(vp_, sp, ip, n_rows, H, D, op, lp,
                                 _stream_handle(stream, dev)))
+
+
+# ------------------------------------------------------- graph-capturable --
+
+class DecodeGraph:
+    """A fixed-capacity decode planned on the device (``bia_decode_graph*``):
+    its runs make no host-to-device copy and allocate nothing, so they can be
+    captured in a HIP graph and replayed with new buffer contents."""
+
+    def __init__(self, handle, max_batch, num_qo_heads, num_kv_heads, head_dim, num_pages,
+                 max_kv_len, page_table_capacity, split_size):
+        self._h = handle
+        self.max_batch = max_batch
+        self.num_qo_heads = num_qo_heads
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.num_pages = num_pages
+        self.max_kv_len = max_kv_len
+        self.page_table_capacity = page_table_capacity
+        self.split_size = split_size
+        self.workspace_bytes = int(load_library().bia_decode_graph_workspace_bytes(handle))
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise BiaError(1, "decode graph already destroyed")
+        return self._h
+
+    def close(self):
+        if self._h is not None:
+            load_library().bia_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def bia_decode_graph_create(*, max_batch, num_qo_heads, num_kv_heads, head_dim, num_pages,
+                            max_kv_len, page_table_capacity, split_size=BIA_DECODE_SPLIT,
+                            page_size: int = BIA_PAGE_SIZE) -> DecodeGraph:
+    handle = ctypes.c_void_p()
+    _check(load_library().bia_decode_graph_create(
+        max_batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, max_kv_len,
+        page_table_capacity, split_size, ctypes.byref(handle)))
+    return DecodeGraph(handle.value, max_batch, num_qo_heads, num_kv_heads, head_dim,
+                       num_pages, max_kv_len, page_table_capacity, split_size)
+
+
+def bia_decode_graph_workspace_bytes(dg: DecodeGraph) -> int:
+    return int(load_library().bia_decode_graph_workspace_bytes(dg.handle))
+
+
+def bia_decode_graph_destroy(dg: DecodeGraph):
+    dg.close()
+
+
+def bia_decode_graph_run(dg: DecodeGraph, batch, kv_indptr_dev, q, k_pool, v_pool,
+                         page_table_dev, sm_scale, out, lse, workspace, stream=None):
+    """Decode of ``batch`` requests without host planning (see
+    ``bia_decode_graph_run`` in bia.h). ``kv_indptr_dev`` is a device int32
+    tensor of ``batch + 1`` cumulative kv lengths; ``page_table_dev`` holds at
+    least ``page_table_capacity`` entries."""
+    torch = _torch()
+    if not 0 <= batch <= dg.max_batch:
+        raise BiaError(2, f"batch {batch} outside [0, {dg.max_batch}]")
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    bf16 = torch.bfloat16
+    Hq, Hkv, D = dg.num_qo_heads, dg.num_kv_heads, dg.head_dim
+    ip = _dev_ptr(kv_indptr_dev, "kv_indptr_dev", torch.int32, (batch + 1,), device=dev)
+    qp = _dev_ptr(q, "q", bf16, (batch, Hq, D), device=dev)
+    pool_shape = (dg.num_pages, BIA_PAGE_SIZE, Hkv, D)
+    kp = _dev_ptr(k_pool, "k_pool", bf16, pool_shape, device=dev)
+    vp = _dev_ptr(v_pool, "v_pool", bf16, pool_shape, device=dev)
+    ptp = _dev_ptr(page_table_dev, "page_table_dev", torch.int32,
+                   min_numel=dg.page_table_capacity, device=dev)
+    op = _dev_ptr(out, "out", bf16, (batch, Hq, D), device=dev)
+    lp = None if lse is None else _dev_ptr(lse, "lse", torch.float32, (batch, Hq), device=dev)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, min_numel=dg.workspace_bytes,
+                  device=dev)
+    _check(load_library().bia_decode_graph_run(
+        ctypes.c_void_p(dg.handle), batch, ip, qp, kp, vp, ptp, float(sm_scale), op, lp, wp,
+        workspace.numel(), _stream_handle(stream, q.device)))
+
+
+def bia_decode_graph_read_flags(dg: DecodeGraph, workspace, batch, stream=None) -> np.ndarray:
+    """Per-request flags of the last run on ``workspace`` (0 = valid; 1 kv_len
+    out of range, 2 pages past the table capacity, 4 a page id outside the
+    pool). Waits for the stream."""
+    torch = _torch()
+    flags = np.zeros(max(batch, 1), dtype=np.int32)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, min_numel=dg.workspace_bytes)
+    _check(load_library().bia_decode_graph_read_flags(
+        ctypes.c_void_p(dg.handle), wp, batch, _ptr_i32(flags),
+        _stream_handle(stream, workspace.device)))
+    return flags[:batch]

@@ -636,6 +636,7 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   __shared__ float sm_o[4][G][D];
 
   const WorkItem it = items[blockIdx.x];
+  if (it.n_tok == 0) return;  // a fixed-capacity slot past the request's partitions
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -930,6 +931,87 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Device planner of the fixed-capacity (graph-capturable) decode. Workgroup r
+// reads request r's kv_len from the device kv_indptr, sums the page counts of
+// the requests before it for its page offset, checks the request, and writes
+// its work items and merges in the form the host planner gives them: kv head
+// h's partition s at item (r * Hkv + h) * max_splits + s, with partial-state
+// slots ((r * Hkv + h) * max_splits + s) * g + head-in-group, and its merge at
+// r * Hkv + h. Slots past the request's partitions get n_tok = 0 (the decode
+// kernel returns at once; the merge kernel has no rows). flags[r] is 0 for a
+// valid request, else a reason bit; an invalid request reads no keys and its
+// rows come out as the empty state (o = 0, lse = -inf).
+// ---------------------------------------------------------------------------
+constexpr int32_t kGraphBadKvLen = 1;  // kv_len < 1 or > max_kv_len
+constexpr int32_t kGraphBadTable = 2;  // pages past page_table_capacity
+constexpr int32_t kGraphBadPage = 4;   // a page id outside [0, num_pages)
+
+__global__ void __launch_bounds__(kThreads)
+decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
+                         const int32_t* __restrict__ page_table, int num_kv_heads, int group,
+                         int split, int max_splits, int max_kv_len, int num_pages,
+                         int page_table_capacity, int32_t* __restrict__ flags,
+                         WorkItem* __restrict__ items, MergeItem* __restrict__ merges) {
+  __shared__ int64_t sm_sum[kThreads];
+  __shared__ int32_t sm_bad;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t part = 0;
+  for (int q = tid; q < r; q += kThreads) {
+    const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
+    part += len > 0 ? (len + 15) / 16 : 0;
+  }
+  sm_sum[tid] = part;
+  if (tid == 0) sm_bad = 0;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {  // integer sums: exact in any order
+    if (tid < w) sm_sum[tid] += sm_sum[tid + w];
+    __syncthreads();
+  }
+  const int64_t page_off = sm_sum[0];
+  const int64_t kv_len = static_cast<int64_t>(kv_indptr[r + 1]) - kv_indptr[r];
+  int32_t bad = 0;
+  if (kv_len < 1 || kv_len > max_kv_len) bad = kGraphBadKvLen;
+  const int64_t n_pages = bad ? 0 : (kv_len + 15) / 16;
+  if (!bad && page_off + n_pages > page_table_capacity) bad = kGraphBadTable;
+  if (!bad) {
+    bool any = false;
+    for (int64_t i = tid; i < n_pages; i += kThreads) {
+      const int32_t pid = page_table[page_off + i];
+      any = any || pid < 0 || pid >= num_pages;
+    }
+    if (any) sm_bad = kGraphBadPage;  // every writer stores the same value
+  }
+  __syncthreads();
+  if (!bad) bad = sm_bad;
+  const int32_t n_splits = bad ? 1 : static_cast<int32_t>((kv_len - 1) / split + 1);
+  if (tid == 0) flags[r] = bad;
+  for (int t = tid; t < num_kv_heads * max_splits; t += kThreads) {
+    const int h = t / max_splits;
+    const int sp = t % max_splits;
+    const int64_t idx = (static_cast<int64_t>(r) * num_kv_heads + h) * max_splits + sp;
+    WorkItem w{r, 0, 0, 0, 0, h, 0, -1};
+    if (sp < n_splits) {
+      w.n_tok = 1;
+      if (!bad) {
+        w.pos0 = static_cast<int32_t>(kv_len - 1);
+        w.kv_len = static_cast<int32_t>(kv_len);
+        w.page_off = static_cast<int32_t>(page_off);
+        w.kv_begin = sp * split;
+        w.state = n_splits > 1 ? static_cast<int32_t>(idx * group) : -1;
+      }
+    }
+    items[idx] = w;
+  }
+  for (int h = tid; h < num_kv_heads; h += kThreads) {
+    const int64_t base = (static_cast<int64_t>(r) * num_kv_heads + h) * max_splits * group;
+    merges[static_cast<int64_t>(r) * num_kv_heads + h] =
+        MergeItem{static_cast<int32_t>(base), n_splits > 1 ? n_splits : 0, r,
+                  n_splits > 1 ? 1 : 0, h, group, 0, 0};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch layer.
 // ---------------------------------------------------------------------------
 std::mutex g_pin_mutex;
@@ -983,38 +1065,53 @@ bia_status upload(const bia_plan* plan, void* workspace, hipStream_t stream) {
   return BIA_OK;
 }
 
+// Where a decode or merge launch finds its work list and partial states.
+struct ListLaunch {
+  const unsigned char* items;  // WorkItem[] or MergeItem[] in the workspace
+  unsigned n;                  // workgroups to launch
+  int num_qo_heads, num_kv_heads, group, split;
+  float* o_part;
+  float* lse_part;
+};
+
+ListLaunch plan_items(const bia::PlanData& d, unsigned char* ws) {
+  return ListLaunch{ws + d.off_items, static_cast<unsigned>(d.items.size()), d.num_qo_heads,
+                    d.num_kv_heads, d.group, d.split, reinterpret_cast<float*>(ws + d.off_o),
+                    reinterpret_cast<float*>(ws + d.off_lse)};
+}
+
+ListLaunch plan_merges(const bia::PlanData& d, unsigned char* ws) {
+  ListLaunch L = plan_items(d, ws);
+  L.items = ws + d.off_merges;
+  L.n = static_cast<unsigned>(d.merges.size());
+  return L;
+}
+
 template <int D>
-void launch_merge_tiles(const bia::PlanData& d, unsigned char* ws, uint16_t* out, float* lse,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(merge_tiles_kernel<D>, dim3(static_cast<unsigned>(d.merges.size())),
-                     dim3(kThreads), 0, stream,
-                     reinterpret_cast<const MergeItem*>(ws + d.off_merges),
-                     reinterpret_cast<const float*>(ws + d.off_o),
-                     reinterpret_cast<const float*>(ws + d.off_lse), d.num_qo_heads,
-                     log2_exact(d.group), out, lse);
+void launch_merge_tiles(const ListLaunch& L, uint16_t* out, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_tiles_kernel<D>, dim3(L.n), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const MergeItem*>(L.items), L.o_part, L.lse_part,
+                     L.num_qo_heads, log2_exact(L.group), out, lse);
 }
 
 template <int D, int G>
-void launch_decode(const bia::PlanData& d, unsigned char* ws, const uint16_t* q,
-                   const uint16_t* kp, const uint16_t* vp, const int32_t* pt, float scale_log2,
-                   uint16_t* out, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(static_cast<unsigned>(d.items.size())),
-                     dim3(kThreads), 0, stream,
-                     reinterpret_cast<const WorkItem*>(ws + d.off_items), q, kp, vp, pt,
-                     scale_log2, d.num_qo_heads, d.num_kv_heads, d.split, out, lse,
-                     reinterpret_cast<float*>(ws + d.off_o),
-                     reinterpret_cast<float*>(ws + d.off_lse));
+void launch_decode(const ListLaunch& L, const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
+                   const int32_t* pt, float scale_log2, uint16_t* out, float* lse,
+                   hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(L.n), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const WorkItem*>(L.items), q, kp, vp, pt, scale_log2,
+                     L.num_qo_heads, L.num_kv_heads, L.split, out, lse, L.o_part, L.lse_part);
 }
 
 template <int D>
-void launch_decode_g(const bia::PlanData& d, unsigned char* ws, const uint16_t* q,
-                     const uint16_t* kp, const uint16_t* vp, const int32_t* pt,
-                     float scale_log2, uint16_t* out, float* lse, hipStream_t stream) {
-  switch (d.group) {
-    case 1: launch_decode<D, 1>(d, ws, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-    case 2: launch_decode<D, 2>(d, ws, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-    case 4: launch_decode<D, 4>(d, ws, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-    default: launch_decode<D, 8>(d, ws, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+void launch_decode_g(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
+                     const uint16_t* vp, const int32_t* pt, float scale_log2, uint16_t* out,
+                     float* lse, hipStream_t stream) {
+  switch (L.group) {
+    case 1: launch_decode<D, 1>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+    case 2: launch_decode<D, 2>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+    case 4: launch_decode<D, 4>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+    default: launch_decode<D, 8>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
   }
 }
 
@@ -1058,9 +1155,9 @@ extern "C" bia_status bia_prefill_paged(const bia_plan* plan, const void* q, con
   }
   if (!d.merges.empty()) {
     if (d.head_dim == 128)
-      launch_merge_tiles<128>(d, ws, o, lse, stream);
+      launch_merge_tiles<128>(plan_merges(d, ws), o, lse, stream);
     else
-      launch_merge_tiles<64>(d, ws, o, lse, stream);
+      launch_merge_tiles<64>(plan_merges(d, ws), o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -1085,14 +1182,16 @@ extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, cons
   const auto* vp = static_cast<const uint16_t*>(v_pool);
   auto* o = static_cast<uint16_t*>(out);
   if (d.head_dim == 128)
-    launch_decode_g<128>(d, ws, qq, kp, vp, page_table_dev, scale_log2, o, lse, stream);
+    launch_decode_g<128>(plan_items(d, ws), qq, kp, vp, page_table_dev, scale_log2, o, lse,
+                         stream);
   else
-    launch_decode_g<64>(d, ws, qq, kp, vp, page_table_dev, scale_log2, o, lse, stream);
+    launch_decode_g<64>(plan_items(d, ws), qq, kp, vp, page_table_dev, scale_log2, o, lse,
+                        stream);
   if (!d.merges.empty()) {
     if (d.head_dim == 128)
-      launch_merge_tiles<128>(d, ws, o, lse, stream);
+      launch_merge_tiles<128>(plan_merges(d, ws), o, lse, stream);
     else
-      launch_merge_tiles<64>(d, ws, o, lse, stream);
+      launch_merge_tiles<64>(plan_merges(d, ws), o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -1156,5 +1255,78 @@ extern "C" bia_status bia_append_paged_kv(const bia_plan* plan, const void* k_ne
                      static_cast<uint16_t*>(v_pool));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  return BIA_OK;
+}
+
+extern "C" bia_status bia_decode_graph_run(const bia_decode_graph* dg, int32_t batch,
+                                           const int32_t* kv_indptr_dev, const void* q,
+                                           const void* k_pool, const void* v_pool,
+                                           const int32_t* page_table_dev, float sm_scale,
+                                           void* out, float* lse, void* workspace,
+                                           size_t workspace_bytes, void* stream_handle) {
+  if (dg == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "decode graph handle is NULL");
+  const bia::DecodeGraphData& d = dg->d;
+  if (batch < 0 || batch > d.max_batch)
+    return bia::fail(BIA_ERR_SHAPE, "batch %d outside [0, %d]", batch, d.max_batch);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return bia::fail(BIA_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  if (batch == 0) return BIA_OK;
+  if (kv_indptr_dev == nullptr || q == nullptr || k_pool == nullptr || v_pool == nullptr ||
+      page_table_dev == nullptr || out == nullptr)
+    return bia::fail(BIA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (workspace == nullptr || workspace_bytes < d.ws_bytes)
+    return bia::fail(BIA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed",
+                     workspace == nullptr ? size_t(0) : workspace_bytes, d.ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % bia::kWsAlign != 0)
+    return bia::fail(BIA_ERR_WORKSPACE, "workspace is not %zu-byte aligned", bia::kWsAlign);
+  hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  auto* flags = reinterpret_cast<int32_t*>(ws + d.off_flags);
+  auto* items = reinterpret_cast<WorkItem*>(ws + d.off_items);
+  auto* merges = reinterpret_cast<MergeItem*>(ws + d.off_merges);
+  hipLaunchKernelGGL(decode_graph_plan_kernel, dim3(static_cast<unsigned>(batch)),
+                     dim3(kThreads), 0, stream, kv_indptr_dev, page_table_dev, d.num_kv_heads,
+                     d.group, d.split, d.max_splits, d.max_kv_len, d.num_pages,
+                     d.page_table_capacity, flags, items, merges);
+  ListLaunch L{ws + d.off_items,
+               static_cast<unsigned>(int64_t(batch) * d.num_kv_heads * d.max_splits),
+               d.num_qo_heads, d.num_kv_heads, d.group, d.split,
+               reinterpret_cast<float*>(ws + d.off_o), reinterpret_cast<float*>(ws + d.off_lse)};
+  const float scale_log2 = sm_scale * kLog2e;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kp = static_cast<const uint16_t*>(k_pool);
+  const auto* vp = static_cast<const uint16_t*>(v_pool);
+  auto* o = static_cast<uint16_t*>(out);
+  if (d.head_dim == 128)
+    launch_decode_g<128>(L, qq, kp, vp, page_table_dev, scale_log2, o, lse, stream);
+  else
+    launch_decode_g<64>(L, qq, kp, vp, page_table_dev, scale_log2, o, lse, stream);
+  if (d.max_splits > 1) {
+    L.items = ws + d.off_merges;
+    L.n = static_cast<unsigned>(int64_t(batch) * d.num_kv_heads);
+    if (d.head_dim == 128)
+      launch_merge_tiles<128>(L, o, lse, stream);
+    else
+      launch_merge_tiles<64>(L, o, lse, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode graph launch");
+  return BIA_OK;
+}
+
+extern "C" bia_status bia_decode_graph_read_flags(const bia_decode_graph* dg,
+                                                  const void* workspace, int32_t batch,
+                                                  int32_t* flags_host, void* stream_handle) {
+  if (dg == nullptr || workspace == nullptr || flags_host == nullptr)
+    return bia::fail(BIA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (batch < 0 || batch > dg->d.max_batch)
+    return bia::fail(BIA_ERR_SHAPE, "batch %d outside [0, %d]", batch, dg->d.max_batch);
+  if (batch == 0) return BIA_OK;
+  hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+  const auto* src = static_cast<const unsigned char*>(workspace) + dg->d.off_flags;
+  hipError_t e = hipMemcpyAsync(flags_host, src, size_t(batch) * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading decode graph flags");
   return BIA_OK;
 }

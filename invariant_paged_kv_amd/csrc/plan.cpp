@@ -107,20 +107,10 @@ static bia_status build(PlanData& d, const int32_t* qo_indptr,
 
 using namespace bia;
 
-extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
-                                      const int32_t* kv_indptr,
-                                      const int32_t* page_table, int32_t batch,
-                                      int32_t num_qo_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t page_size,
-                                      int32_t num_pages, int32_t split_size,
-                                      uint32_t flags, bia_plan** out_plan) {
-  if (out_plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out_plan is NULL");
-  *out_plan = nullptr;
-  if (mode != BIA_MODE_PREFILL && mode != BIA_MODE_DECODE)
-    return fail(BIA_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
-  if (batch < 0) return fail(BIA_ERR_INVALID_ARG, "batch %d < 0", batch);
-  if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
-    return fail(BIA_ERR_INVALID_ARG, "qo_indptr / kv_indptr is NULL");
+// Head counts, head dim, page size, pool size and split size every plan kind
+// shares.
+static bia_status check_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_pages, int32_t split_size) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0)
     return fail(BIA_ERR_INVALID_ARG, "head counts must be positive (%d, %d)",
                 num_qo_heads, num_kv_heads);
@@ -139,6 +129,27 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
     return fail(BIA_ERR_INVALID_ARG,
                 "split_size %d must be a positive multiple of the %d-key KV tile",
                 split_size, kKvTile);
+  return BIA_OK;
+}
+
+extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
+                                      const int32_t* kv_indptr,
+                                      const int32_t* page_table, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size,
+                                      int32_t num_pages, int32_t split_size,
+                                      uint32_t flags, bia_plan** out_plan) {
+  if (out_plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out_plan is NULL");
+  *out_plan = nullptr;
+  if (mode != BIA_MODE_PREFILL && mode != BIA_MODE_DECODE)
+    return fail(BIA_ERR_INVALID_ARG, "unknown mode %d", static_cast<int>(mode));
+  if (batch < 0) return fail(BIA_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
+    return fail(BIA_ERR_INVALID_ARG, "qo_indptr / kv_indptr is NULL");
+  const bia_status shape_st =
+      check_shape(num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, split_size);
+  if (shape_st != BIA_OK) return shape_st;
+  const int32_t group = num_qo_heads / num_kv_heads;
 
   if ((flags & ~BIA_PLAN_STRICT_CHUNK_ALIGN) != 0)
     return fail(BIA_ERR_INVALID_ARG, "unknown plan flags 0x%x", flags);
@@ -241,6 +252,61 @@ extern "C" int32_t bia_plan_get_items(const bia_plan* plan, int32_t* items, int3
 extern "C" int64_t bia_plan_num_states(const bia_plan* plan) {
   return plan == nullptr ? 0 : plan->d.n_states;
 }
+
+extern "C" bia_status bia_decode_graph_create(int32_t max_batch, int32_t num_qo_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t page_size, int32_t num_pages,
+                                              int32_t max_kv_len, int32_t page_table_capacity,
+                                              int32_t split_size, bia_decode_graph** out) {
+  if (out == nullptr) return fail(BIA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const bia_status shape_st =
+      check_shape(num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, split_size);
+  if (shape_st != BIA_OK) return shape_st;
+  if (max_batch <= 0) return fail(BIA_ERR_INVALID_ARG, "max_batch %d must be positive", max_batch);
+  if (max_kv_len <= 0)
+    return fail(BIA_ERR_INVALID_ARG, "max_kv_len %d must be positive", max_kv_len);
+  if (page_table_capacity < 0)
+    return fail(BIA_ERR_INVALID_ARG, "page_table_capacity %d < 0", page_table_capacity);
+  const int32_t group = num_qo_heads / num_kv_heads;
+  const int64_t max_splits = ceil_div(max_kv_len, split_size);
+  const int64_t n_items = int64_t(max_batch) * num_kv_heads * max_splits;
+  const int64_t n_states = n_items * group;
+  if (n_items > INT32_MAX || n_states > INT32_MAX)
+    return fail(BIA_ERR_SHAPE, "capacity needs %lld partial states (> 2^31)",
+                static_cast<long long>(n_states));
+  bia_decode_graph* dg = new (std::nothrow) bia_decode_graph();
+  if (dg == nullptr) return fail(BIA_ERR_INVALID_ARG, "out of host memory");
+  DecodeGraphData& d = dg->d;
+  d.max_batch = max_batch;
+  d.num_qo_heads = num_qo_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = head_dim;
+  d.page_size = page_size;
+  d.num_pages = num_pages;
+  d.max_kv_len = max_kv_len;
+  d.page_table_capacity = page_table_capacity;
+  d.split = split_size;
+  d.group = group;
+  d.max_splits = static_cast<int32_t>(max_splits);
+  d.n_items = n_items;
+  d.n_merges = int64_t(max_batch) * num_kv_heads;
+  d.n_states = n_states;
+  d.off_flags = 0;
+  d.off_items = align_up(size_t(max_batch) * sizeof(int32_t), kWsAlign);
+  d.off_merges = align_up(d.off_items + size_t(n_items) * sizeof(WorkItem), kWsAlign);
+  d.off_o = align_up(d.off_merges + size_t(d.n_merges) * sizeof(MergeItem), kWsAlign);
+  d.off_lse = align_up(d.off_o + size_t(n_states) * head_dim * sizeof(float), kWsAlign);
+  d.ws_bytes = align_up(d.off_lse + size_t(n_states) * sizeof(float), kWsAlign);
+  *out = dg;
+  return BIA_OK;
+}
+
+extern "C" size_t bia_decode_graph_workspace_bytes(const bia_decode_graph* dg) {
+  return dg == nullptr ? 0 : dg->d.ws_bytes;
+}
+
+extern "C" void bia_decode_graph_destroy(bia_decode_graph* dg) { delete dg; }
 
 extern "C" int32_t bia_prefill_chunk_align(void) { return kQTileRows; }
 

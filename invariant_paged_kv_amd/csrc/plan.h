@@ -71,12 +71,29 @@ struct PlanData {
 void set_error(const char* fmt, ...);
 bia_status fail(bia_status st, const char* fmt, ...);
 
+// Fixed-capacity decode planned on the device (graph-capturable). Request r
+// of a call has kv head h's partition s at item (r * Hkv + h) * max_splits + s
+// and its merge at r * Hkv + h; partition s of (r, h) keeps its partial states
+// at slots ((r * Hkv + h) * max_splits + s) * group + head-in-group.
+struct DecodeGraphData {
+  int32_t max_batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages;
+  int32_t max_kv_len, page_table_capacity, split, group, max_splits;
+  // Workspace layout (byte offsets): int32 flags[max_batch] | items | merges |
+  // fp32 o[n_states][head_dim] | fp32 lse[n_states].
+  int64_t n_items, n_merges, n_states;
+  size_t off_flags, off_items, off_merges, off_o, off_lse, ws_bytes;
+};
+
 }  // namespace bia
 
-// The opaque handle of the C ABI.
+// The opaque handles of the C ABI.
 struct bia_plan {
   bia::PlanData d;
   void* pinned = nullptr;  // pinned copy of d.blob, made by the launch layer
+};
+
+struct bia_decode_graph {
+  bia::DecodeGraphData d;
 };
 
 #endif  // BIA_PLAN_INTERNAL_H_

@@ -35,7 +35,10 @@ def test_python_binding_has_every_entry_point():
     """The binding keeps the C names of the calls a user makes."""
     for name in ["bia_plan_create", "bia_plan_destroy", "bia_plan_workspace_bytes",
                  "bia_prefill_paged", "bia_decode_paged", "bia_merge_states",
-                 "bia_prefill_chunk_align", "bia_last_error"]:
+                 "bia_prefill_chunk_align", "bia_last_error", "bia_append_paged_kv",
+                 "bia_decode_graph_create", "bia_decode_graph_destroy",
+                 "bia_decode_graph_workspace_bytes", "bia_decode_graph_run",
+                 "bia_decode_graph_read_flags"]:
         assert name in declared_functions()
         assert callable(getattr(bia, name)), name
 
@@ -243,3 +246,79 @@ def test_append_items_in_workspace():
     assert a.workspace_bytes >= 2 * 32 + 16     # 1 tile item (g=4: 32 tokens) + 1 append
     assert b.workspace_bytes >= 32 + 2 * 16     # 1 tile item + 2 appends
     assert c.workspace_bytes >= 32 + 16
+
+
+# ----------------------------------------------------- graph-capturable decode --
+
+GRAPH = dict(max_batch=64, num_qo_heads=32, num_kv_heads=8, head_dim=128, num_pages=1024,
+             max_kv_len=32768, page_table_capacity=4096, split_size=2048)
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, None),
+    (dict(max_batch=0), "BIA_ERR_INVALID_ARG"),
+    (dict(max_kv_len=0), "BIA_ERR_INVALID_ARG"),
+    (dict(page_table_capacity=-1), "BIA_ERR_INVALID_ARG"),
+    (dict(split_size=100), "BIA_ERR_INVALID_ARG"),
+    (dict(head_dim=96), "BIA_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=48, num_kv_heads=3), "BIA_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=6, num_kv_heads=4), "BIA_ERR_SHAPE"),
+    (dict(page_size=32), "BIA_ERR_UNSUPPORTED"),
+    (dict(max_batch=1 << 20, max_kv_len=1 << 30), "BIA_ERR_SHAPE"),   # > 2^31 states
+])
+def test_decode_graph_validation(change, status):
+    args = dict(GRAPH, **change)
+    if status is None:
+        dg = bia.bia_decode_graph_create(**args)
+        dg.close()
+        return
+    with pytest.raises(bia.BiaError) as e:
+        bia.bia_decode_graph_create(**args)
+    assert status in str(e.value)
+
+
+def test_decode_graph_workspace_layout():
+    """Flags, a fixed item per (request, kv head, partition), a merge per
+    (request, kv head), then fp32 o and lse of every partial-state slot."""
+    dg = bia.bia_decode_graph_create(**GRAPH)
+    max_splits = 32768 // 2048
+    items = 64 * 8 * max_splits
+    states = items * 4
+    def up(x):
+        return (x + 255) // 256 * 256
+    off_items = up(64 * 4)
+    off_merges = up(off_items + items * 32)
+    off_o = up(off_merges + 64 * 8 * 32)
+    off_lse = up(off_o + states * 128 * 4)
+    assert dg.workspace_bytes == up(off_lse + states * 4)
+    dg.close()
+    one = bia.bia_decode_graph_create(**dict(GRAPH, max_kv_len=2048))
+    assert one.workspace_bytes < dg.workspace_bytes
+    one.close()
+
+
+def test_decode_graph_run_host_checks():
+    """Checks that run before anything is enqueued (no GPU needed)."""
+    lib = bia.load_library()
+    dg = bia.bia_decode_graph_create(**GRAPH)
+    h = ctypes.c_void_p(dg.handle)
+    run = lib.bia_decode_graph_run
+    nul = None
+    assert run(None, 1, nul, nul, nul, nul, nul, 1.0, nul, nul, nul, 0, nul) != 0
+    assert "NULL" in bia.bia_last_error()
+    assert _lib._STATUS[run(h, 65, nul, nul, nul, nul, nul, 1.0, nul, nul, nul, 0, nul)] \
+        == "BIA_ERR_SHAPE"
+    assert _lib._STATUS[run(h, -1, nul, nul, nul, nul, nul, 1.0, nul, nul, nul, 0, nul)] \
+        == "BIA_ERR_SHAPE"
+    assert run(h, 0, nul, nul, nul, nul, nul, 1.0, nul, nul, nul, 0, nul) == 0   # no work
+    assert _lib._STATUS[run(h, 0, nul, nul, nul, nul, nul, float("nan"), nul, nul, nul, 0,
+                            nul)] == "BIA_ERR_INVALID_ARG"
+    assert _lib._STATUS[run(h, 2, nul, nul, nul, nul, nul, 1.0, nul, nul, nul, 0, nul)] \
+        == "BIA_ERR_INVALID_ARG"
+    fake = ctypes.c_void_p(0x1000)
+    assert _lib._STATUS[run(h, 2, fake, fake, fake, fake, fake, 1.0, fake, nul, fake, 16,
+                            nul)] == "BIA_ERR_WORKSPACE"
+    flags = np.zeros(1, dtype=np.int32)
+    assert lib.bia_decode_graph_read_flags(None, fake, 1, _lib._ptr_i32(flags), nul) != 0
+    assert lib.bia_decode_graph_read_flags(h, fake, 65, _lib._ptr_i32(flags), nul) != 0
+    dg.close()
