@@ -134,12 +134,116 @@ def cpu_baseline_decode(b, n=8):
                       f"({int(np.diff(kv_ip).sum())} context tokens), same seeded inputs"}
 
 
+def copy_bandwidth(torch, stream, dev, gib=2, reps=10):
+    """Device-to-device copy of a ``gib`` GiB buffer: (read + write bytes) /
+    mean time, GB/s. The achievable-HBM reference the decode is compared to."""
+    n = gib << 29                                   # int16 elements
+    src = torch.ones(n, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t = Timer(torch, stream)
+    for _ in range(reps):
+        s = t.start()
+        dst.copy_(src)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del src, dst
+    return 2.0 * (n * 2) / (ms * 1e-3) / 1e9
+
+
+def decode_sweep(torch, bia, W, db, d_pt, stream, dev, sizes=(1, 8, 16, 32, 64), reps=20):
+    """Planned decode of the first B requests of the B = 64 batch (same pool),
+    with a 512 MB scratch write between calls so small batches are not served
+    from the 256 MB last-level cache. GB/s and ms per call."""
+    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    rows = []
+    for B in sizes:
+        kv = db.kv_indptr[: B + 1]
+        n_pages = int(((np.diff(kv) + 15) // 16).sum())
+        sub = W.PagedBatch(db.qo_indptr[: B + 1], kv, db.page_table[:n_pages], db.num_pages,
+                           db.page_size, db.num_qo_heads, db.num_kv_heads, db.head_dim,
+                           db.sm_scale, db.q[:B].contiguous(), db.k_pool, db.v_pool)
+        plan = bia.bia_plan_create(bia.BIA_MODE_DECODE, sub.qo_indptr, sub.kv_indptr,
+                                   sub.page_table, num_pages=sub.num_pages,
+                                   split_size=bia.BIA_DECODE_SPLIT, num_qo_heads=32,
+                                   num_kv_heads=8, head_dim=128)
+        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(sub.q)
+        lse = torch.empty(sub.q.shape[:2], dtype=torch.float32, device=dev)
+        t = Timer(torch, stream)
+        for i in range(reps + 2):
+            scratch.fill_(i & 0xff)
+            s = t.start()
+            bia.bia_decode_paged(plan, sub.q, sub.k_pool, sub.v_pool, d_pt, sub.sm_scale,
+                                 out, lse, ws, stream)
+            t.stop(s)
+        torch.cuda.synchronize()
+        t.pairs = t.pairs[2:]
+        ms = t.mean_ms()
+        by = decode_bytes(sub.kv_lens(), 32, 8, 128)
+        rows.append({"batch": B, "kv_tokens": int(sub.kv_lens().sum()), "ms": round(ms, 4),
+                     "GB/s": round(by / (ms * 1e-3) / 1e9, 1)})
+        plan.close()
+    del scratch
+    return rows
+
+
+def decode_graph_replay(torch, bia, db, d_pt, stream, dev, ref_out, ref_lse, reps=20):
+    """The graph-capturable decode of the B = 64 batch, captured once in a HIP
+    graph and replayed: ms per replay, GB/s, and whether its bits equal the
+    planned decode's."""
+    B = db.batch
+    dg = bia.bia_decode_graph_create(max_batch=B, num_qo_heads=32, num_kv_heads=8,
+                                     head_dim=128, num_pages=db.num_pages,
+                                     max_kv_len=32768, page_table_capacity=int(d_pt.numel()))
+    ind = torch.as_tensor(db.kv_indptr, dtype=torch.int32, device=dev)
+    out = torch.empty_like(db.q)
+    lse = torch.empty(db.q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(dg.workspace_bytes, dtype=torch.uint8, device=dev)
+
+    def call():
+        bia.bia_decode_graph_run(dg, B, ind, db.q, db.k_pool, db.v_pool, d_pt, db.sm_scale,
+                                 out, lse, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    out.zero_()
+    cur = torch.cuda.current_stream(dev)
+    t = Timer(torch, cur)
+    for i in range(reps + 2):
+        s = t.start()
+        g.replay()
+        t.stop(s)
+    torch.cuda.synchronize()
+    t.pairs = t.pairs[2:]
+    ms = t.mean_ms()
+    same = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and
+                torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)))
+    by = decode_bytes(db.kv_lens(), 32, 8, 128)
+    del g
+    dg.close()
+    return {"ms": round(ms, 4), "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+            "bit_equal_to_planned": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode batch sweep, the graph-replay decode and the "
+                         "copy-bandwidth reference")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy a 1 GiB buffer 3 times, so a counter run also "
                          "records a plain copy of known size (HBM-byte calibration)")
@@ -229,6 +333,11 @@ def main():
 
     invariant = bool(torch.equal(ref_p.view(torch.int16), p_out.view(torch.int16)) and
                      torch.equal(ref_d.view(torch.int16), d_out.view(torch.int16)))
+    extras = {}
+    if not args.no_extras:
+        extras["copy_gbs"] = copy_bandwidth(torch, stream, dev)
+        extras["sweep"] = decode_sweep(torch, bia, W, db, d_pt, stream, dev)
+        extras["graph"] = decode_graph_replay(torch, bia, db, d_pt, stream, dev, d_out, d_lse)
 
     p_flops = prefill_flops(pb.qo_lens(), pb.kv_lens(), 32, 128)
     d_bytes = decode_bytes(db.kv_lens(), 32, 8, 128)
@@ -279,6 +388,14 @@ def main():
         },
         "bit_invariant_across_steps": invariant,
     }
+    if extras:
+        copy = extras["copy_gbs"]
+        result["copy_bandwidth"] = {
+            "value": round(copy, 1), "unit": "GB/s",
+            "what": "2 GiB device-to-device copy, (read + write bytes) / time"}
+        result["decode"]["frac_of_copy"] = round(d_gbs / copy, 4)
+        result["decode"]["sweep"] = extras["sweep"]
+        result["decode"]["graph_replay"] = extras["graph"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(pb)
         result["decode"]["cpu_baseline"] = cpu_baseline_decode(db)

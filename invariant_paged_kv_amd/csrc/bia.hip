@@ -934,13 +934,26 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 // Device planner of the fixed-capacity (graph-capturable) decode. Workgroup r
 // reads request r's kv_len from the device kv_indptr, sums the page counts of
 // the requests before it for its page offset, checks the request, and writes
-// its work items and merges in the form the host planner gives them: kv head
-// h's partition s at item (r * Hkv + h) * max_splits + s, with partial-state
-// slots ((r * Hkv + h) * max_splits + s) * g + head-in-group, and its merge at
-// r * Hkv + h. Slots past the request's partitions get n_tok = 0 (the decode
-// kernel returns at once; the merge kernel has no rows). flags[r] is 0 for a
-// valid request, else a reason bit; an invalid request reads no keys and its
-// rows come out as the empty state (o = 0, lse = -inf).
+// its work items and merges in the form the host planner gives them. Kv head
+// h's partition s keeps its partial states at slots
+// ((r * Hkv + h) * max_splits + s) * g + head-in-group; the request's merge is
+// at r * Hkv + h.
+//
+// Launch order (what the host planner's longest-first sort gives, computed
+// from kv_indptr alone by every workgroup): first the whole partitions of all
+// requests, partition-major, then each request's partial last partition, then
+// the empty slots (n_tok = 0: the decode kernel returns at once). Item index =
+// unit * Hkv + h, so consecutive workgroups, which the dispatcher deals
+// round-robin over the XCDs, are different kv heads of one (request,
+// partition); with (request, head, partition) order the XCD would follow the
+// partition index, and the XCDs holding the low partitions every request has
+// would get most of the work.
+//
+// flags[r] is 0 for a valid request, else a reason bit. An invalid request
+// reads no keys: the first of its slots gets an item with kv_len = 0 (its rows
+// come out as the empty state, o = 0 and lse = -inf) and the rest are empty.
+// Its slots are reserved from kv_len alone (one slot if kv_len itself is out
+// of range), which every workgroup can compute.
 // ---------------------------------------------------------------------------
 constexpr int32_t kGraphBadKvLen = 1;  // kv_len < 1 or > max_kv_len
 constexpr int32_t kGraphBadTable = 2;  // pages past page_table_capacity
@@ -952,23 +965,54 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
                          int split, int max_splits, int max_kv_len, int num_pages,
                          int page_table_capacity, int32_t* __restrict__ flags,
                          WorkItem* __restrict__ items, MergeItem* __restrict__ merges) {
-  __shared__ int64_t sm_sum[kThreads];
+  __shared__ int64_t sm_red[4][kThreads];
   __shared__ int32_t sm_bad;
   const int r = blockIdx.x;
+  const int batch = gridDim.x;
   const int tid = threadIdx.x;
-  int64_t part = 0;
-  for (int q = tid; q < r; q += kThreads) {
+  // slots request q reserves: nf whole partitions and np (0 or 1) partial one
+  auto reserve = [&](int q, int32_t& nf, int32_t& np) {
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
-    part += len > 0 ? (len + 15) / 16 : 0;
+    if (len < 1 || len > max_kv_len) {
+      nf = 0;
+      np = 1;
+    } else {
+      nf = static_cast<int32_t>(len / split);
+      np = len % split != 0 ? 1 : 0;
+    }
+  };
+  // integer sums over the requests (exact in any order): pages before r, whole
+  // partitions of all, partial partitions of all and of those before r
+  int64_t pages_before = 0, all_nf = 0, all_np = 0, np_before = 0;
+  for (int q = tid; q < batch; q += kThreads) {
+    const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
+    int32_t nf, np;
+    reserve(q, nf, np);
+    all_nf += nf;
+    all_np += np;
+    if (q < r) {
+      pages_before += len > 0 ? (len + 15) / 16 : 0;
+      np_before += np;
+    }
   }
-  sm_sum[tid] = part;
+  sm_red[0][tid] = pages_before;
+  sm_red[1][tid] = all_nf;
+  sm_red[2][tid] = all_np;
+  sm_red[3][tid] = np_before;
   if (tid == 0) sm_bad = 0;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {  // integer sums: exact in any order
-    if (tid < w) sm_sum[tid] += sm_sum[tid + w];
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sm_red[k][tid] += sm_red[k][tid + w];
+    }
     __syncthreads();
   }
-  const int64_t page_off = sm_sum[0];
+  const int64_t page_off = sm_red[0][0];
+  const int64_t n_full = sm_red[1][0];        // whole-partition units of the launch
+  const int64_t n_used = n_full + sm_red[2][0];
+  const int64_t my_partial_unit = n_full + sm_red[3][0];
+
   const int64_t kv_len = static_cast<int64_t>(kv_indptr[r + 1]) - kv_indptr[r];
   int32_t bad = 0;
   if (kv_len < 1 || kv_len > max_kv_len) bad = kGraphBadKvLen;
@@ -984,24 +1028,47 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   }
   __syncthreads();
   if (!bad) bad = sm_bad;
-  const int32_t n_splits = bad ? 1 : static_cast<int32_t>((kv_len - 1) / split + 1);
   if (tid == 0) flags[r] = bad;
-  for (int t = tid; t < num_kv_heads * max_splits; t += kThreads) {
-    const int h = t / max_splits;
-    const int sp = t % max_splits;
-    const int64_t idx = (static_cast<int64_t>(r) * num_kv_heads + h) * max_splits + sp;
-    WorkItem w{r, 0, 0, 0, 0, h, 0, -1};
-    if (sp < n_splits) {
-      w.n_tok = 1;
-      if (!bad) {
+
+  int32_t nf_r, np_r;
+  reserve(r, nf_r, np_r);
+  const int32_t n_res = nf_r + np_r;          // this request's partitions (= its slots)
+  const int32_t n_splits = bad ? 0 : n_res;
+  for (int sp = tid; sp < n_res; sp += kThreads) {
+    int64_t unit;
+    if (sp < nf_r) {  // whole partition sp: after every whole partition with index < sp,
+                      // and after partition sp of the requests before r
+      unit = 0;
+      for (int q = 0; q < batch; ++q) {
+        int32_t nf, np;
+        reserve(q, nf, np);
+        unit += min(nf, sp) + (q < r && nf > sp ? 1 : 0);
+      }
+    } else {
+      unit = my_partial_unit;
+    }
+#pragma unroll 1
+    for (int h = 0; h < num_kv_heads; ++h) {
+      WorkItem w{r, 0, 0, 0, 0, h, 0, -1};
+      if (bad) {
+        w.n_tok = sp == 0 ? 1 : 0;  // kv_len 0: the empty state
+      } else {
+        const int64_t slot = (static_cast<int64_t>(r) * num_kv_heads + h) * max_splits + sp;
+        w.n_tok = 1;
         w.pos0 = static_cast<int32_t>(kv_len - 1);
         w.kv_len = static_cast<int32_t>(kv_len);
         w.page_off = static_cast<int32_t>(page_off);
         w.kv_begin = sp * split;
-        w.state = n_splits > 1 ? static_cast<int32_t>(idx * group) : -1;
+        w.state = n_splits > 1 ? static_cast<int32_t>(slot * group) : -1;
       }
+      items[unit * num_kv_heads + h] = w;
     }
-    items[idx] = w;
+  }
+  // this workgroup's share of the empty slots after the used ones
+  const int64_t n_units = static_cast<int64_t>(batch) * max_splits;
+  for (int64_t u = n_used + r + static_cast<int64_t>(tid) * batch; u < n_units;
+       u += static_cast<int64_t>(kThreads) * batch) {
+    for (int h = 0; h < num_kv_heads; ++h) items[u * num_kv_heads + h] = WorkItem{r, 0, 0, 0, 0, h, 0, -1};
   }
   for (int h = tid; h < num_kv_heads; h += kThreads) {
     const int64_t base = (static_cast<int64_t>(r) * num_kv_heads + h) * max_splits * group;

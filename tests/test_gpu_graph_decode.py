@@ -138,3 +138,41 @@ def test_invalid_requests_are_flagged():
     alone = W.decode_batch(1, seed=81, num_pages=1024, device=DEV, ctx_lens=ctx[:1])
     o1, l1 = run_decode(alone)
     assert bits_equal(out[:1], o1) and bits_equal(lse[:1], l1)
+
+
+def test_device_plan_matches_host_plan():
+    """The device planner's work list holds the host planner's items (all
+    fields but the partial-state slot), each once, whole partitions first,
+    partial last partitions next, empty slots last."""
+    ctx = [4096, 1, 2048, 2049, 6000, 16384, 100, 12345, 4095]
+    b = W.decode_batch(len(ctx), seed=91, num_pages=4096, device=DEV, ctx_lens=ctx)
+    max_batch, max_kv, cap = 12, 16384, 4096
+    dg = make_dg(b, max_batch, max_kv, cap)
+    ind, pt = device_tables(b, cap)
+    out = torch.empty_like(b.q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=DEV)
+    ws = torch.zeros(dg.workspace_bytes, dtype=torch.uint8, device=DEV)
+    say("graph decode: device plan vs host plan")
+    bia.bia_decode_graph_run(dg, b.batch, ind, b.q, b.k_pool, b.v_pool, pt, b.sm_scale, out,
+                             lse, ws)
+    torch.cuda.synchronize()
+    max_splits = (max_kv + 2047) // 2048
+    off_items = (max_batch * 4 + 255) // 256 * 256
+    n = b.batch * b.num_kv_heads * max_splits
+    dev_items = ws[off_items: off_items + n * 32].view(torch.int32).view(n, 8).cpu().numpy()
+    dg.close()
+    plan = bia.bia_plan_create(bia.BIA_MODE_DECODE, b.qo_indptr, b.kv_indptr, b.page_table,
+                               num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+                               head_dim=b.head_dim, num_pages=b.num_pages, split_size=2048)
+    host_items = plan.items()
+    plan.close()
+    live = dev_items[dev_items[:, 1] > 0]
+    assert len(live) == len(host_items)
+    key = lambda a: sorted(map(tuple, a[:, :7].tolist()))
+    assert key(live) == key(host_items)
+    # order: whole partitions, then partial ones, then the empty slots
+    n_live = len(live)
+    assert (dev_items[n_live:, 1] == 0).all()
+    lens = np.minimum(live[:, 3] - live[:, 6], 2048)
+    whole = lens == 2048
+    assert not whole[np.argmax(~whole):].any() if (~whole).any() else True
