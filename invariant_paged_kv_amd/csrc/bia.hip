@@ -620,8 +620,17 @@ __device__ __forceinline__ void combine_sym(float& m, float& l, float (&o)[N], f
   m = mm;
 }
 
+// Chunks in flight per wave plus one (three register buffers), and the
+// workgroups per CU the registers allow: two up to 4 q heads per kv head; at
+// 8 the accumulators alone take 8 * D / 8 registers a lane, so one workgroup
+// per CU keeps everything in registers (two would spill to scratch).
+template <int G>
+constexpr int kDecodeBuffers = 3;
+template <int G>
+constexpr int kDecodeBlocksPerCU = G <= 4 ? 2 : 1;
+
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, kDecodeBlocksPerCU<G>)
 decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
               const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
               const int32_t* __restrict__ page_table, float scale_log2, int num_qo_heads,
@@ -757,20 +766,28 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
     }
   };
 
-  // This wave's chunks are wave, wave + 4, ...: two register buffers
-  // alternate; page ids run one chunk ahead of the loads that use them.
-  uint32_t ka[2][W], va[2][W], kb2[2][W], vb2[2][W];
-  int c = wave;
-  if (c < n_chunks) load(ka, va, c, page_of(c));
-  int32_t page_next = page_of(c + 4);
-  for (; c < n_chunks; c += 8) {
-    if (c + 4 < n_chunks) load(kb2, vb2, c + 4, page_next);
-    page_next = page_of(c + 8);
-    compute(ka, va, c);
-    if (c + 4 >= n_chunks) break;
-    if (c + 8 < n_chunks) load(ka, va, c + 8, page_next);
-    page_next = page_of(c + 12);
-    compute(kb2, vb2, c + 4);
+  // This wave's chunks are wave, wave + 4, ... in that order. NB register
+  // buffers rotate: while chunk c is computed, the loads of the next NB - 1
+  // chunks are in flight, and page ids run one chunk ahead of the loads that
+  // use them. The order of the arithmetic does not depend on NB.
+  constexpr int NB = kDecodeBuffers<G>;
+  uint32_t kbuf[NB][2][W], vbuf[NB][2][W];
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k) {
+    const int cl = wave + 4 * k;
+    if (cl < n_chunks) load(kbuf[k], vbuf[k], cl, page_of(cl));
+  }
+  int32_t page_next = page_of(wave + 4 * (NB - 1));
+  for (int c = wave; c < n_chunks; c += 4 * NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int cc = c + 4 * k;
+      if (cc >= n_chunks) break;  // uniform over the wave
+      const int cl = cc + 4 * (NB - 1);
+      if (cl < n_chunks) load(kbuf[(k + NB - 1) % NB], vbuf[(k + NB - 1) % NB], cl, page_next);
+      page_next = page_of(cl + 4);
+      compute(kbuf[k], vbuf[k], cc);
+    }
   }
 
   // ---- combine the 8 key groups of the wave (butterfly over lane ^ 8, 16, 32) ----

@@ -86,6 +86,8 @@ def test_ragged_prefill(heads, split):
     dict(num_qo_heads=8, num_kv_heads=8, head_dim=128),
     dict(num_qo_heads=16, num_kv_heads=2, head_dim=64),
     dict(num_qo_heads=16, num_kv_heads=4, head_dim=128),
+    dict(num_qo_heads=64, num_kv_heads=8, head_dim=128),
+    dict(num_qo_heads=16, num_kv_heads=8, head_dim=128),
 ], ids=lambda h: f"hq{h['num_qo_heads']}_hkv{h['num_kv_heads']}_d{h['head_dim']}")
 def test_decode_small(heads):
     say(f"decode small {heads}")
