@@ -878,13 +878,29 @@ merge_tiles_kernel(const MergeItem* __restrict__ merges, const float* __restrict
   const int g = 1 << group_shift;
   const int rows = mi.n_tok * g;
   const int d0 = (threadIdx.x % TPR) * 4;
+  constexpr int kBatch = 8;  // states loaded ahead of their fold
   for (int x = threadIdx.x / TPR; x < rows; x += RPP) {
     float M = kNegInf, sum = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < mi.n_splits; ++k) {
-      const int64_t st = static_cast<int64_t>(mi.state0) + static_cast<int64_t>(k) * mi.stride + x;
-      const float4 v = *reinterpret_cast<const float4*>(o_part + st * D + d0);
-      const float ok[4] = {v.x, v.y, v.z, v.w};
-      fold_state<4>(M, sum, acc, lse_part[st], ok);
+    for (int k0 = 0; k0 < mi.n_splits; k0 += kBatch) {
+      // issue the loads of up to kBatch states, then fold them in order
+      float4 v[kBatch];
+      float l[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (k0 + i < mi.n_splits) {
+          const int64_t st = static_cast<int64_t>(mi.state0) +
+                             static_cast<int64_t>(k0 + i) * mi.stride + x;
+          v[i] = *reinterpret_cast<const float4*>(o_part + st * D + d0);
+          l[i] = lse_part[st];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (k0 + i < mi.n_splits) {
+          const float ok[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          fold_state<4>(M, sum, acc, l[i], ok);
+        }
+      }
     }
     const float lse_nat = fold_finish<4>(M, sum, acc);
     const int tok = x >> group_shift;
