@@ -271,14 +271,19 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   // Instruction r of this wave fills rows row0 .. row0 + RPI - 1 (one page),
   // row0 = RPI * (4 r + wave); lane l takes row row0 + l / SLOTS and puts its
   // 16 bytes in slot l % SLOTS, i.e. chunk (l % SLOTS) ^ swz(row).
-  auto pages = [&](int t, int32_t (&pg)[IPW]) {
-#pragma unroll
-    for (int r = 0; r < IPW; ++r) {
-      // clamped to the item's last key, so the read is always in range; a
-      // page of a row past kv_end is never used
-      const int k0 = min(it.kv_begin + 64 * t + RPI * (4 * r + wave), kv_end - 1);
-      pg[r] = __builtin_amdgcn_readfirstlane(pt[k0 >> 4]);
-    }
+  // Page ids of tile t (its 4 pages) as one vector load, lane l holding page
+  // l % 4 (clamped to the item's last page, so the read is always in range;
+  // a page past kv_end is never used). Vector rather than scalar loads: a
+  // scalar load in flight would make every LDS wait of the tile wait for it
+  // too (the two share a counter, and scalar loads return out of order); the
+  // ids are taken out with readlane only when the tile's DMAs are issued, one
+  // or two tiles later.
+  const int last_page = (kv_end - 1) >> 4;
+  auto pages = [&](int t) -> int32_t {
+    return pt[min(((it.kv_begin + 64 * t) >> 4) + (lane & 3), last_page)];
+  };
+  auto page_id = [&](int32_t pgv, int r) -> int32_t {
+    return __builtin_amdgcn_readlane(pgv, (RPI * (4 * r + wave)) >> 4);
   };
   // A lane's rows within a page and its chunk are the same for every DMA
   // instruction of every tile (row0 is a multiple of 16 apart between
@@ -286,13 +291,14 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int dma_row = RPI * wave + lane / SLOTS;  // row of instruction 0 (mod 16)
   const uint32_t dma_lane_off = static_cast<uint32_t>(
       ((dma_row & 15) * slot_stride + head_off + ((lane % SLOTS) ^ lds_swz<D>(dma_row)) * 8) * 2);
-  auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, const int32_t (&pg)[IPW]) {
+  auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, int32_t pgv) {
     const int t0 = it.kv_begin + 64 * t;
     if (t0 + 64 <= kv_end) {  // uniform: every row of the tile is a key of the item
 #pragma unroll
       for (int r = 0; r < IPW; ++r) {
         const int row0 = RPI * (4 * r + wave);
-        const uint16_t* page_base = pool + static_cast<int64_t>(pg[r]) * 16 * slot_stride;
+        const uint16_t* page_base =
+            pool + static_cast<int64_t>(page_id(pgv, r)) * 16 * slot_stride;
         lds_dma16_sbase(dma_lane_off, page_base, lds_base + buf * TB + row0 * RB);
       }
     } else {
@@ -304,8 +310,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
         const int key = t0 + row;
         const int dst = buf * TB + row0 * RB;
         if (key < kv_end) {
-          const uint16_t* src = pool + (static_cast<int64_t>(pg[r]) * 16 + (key & 15)) *
-                                           slot_stride + head_off + chunk * 8;
+          const uint16_t* src = pool + (static_cast<int64_t>(page_id(pgv, r)) * 16 +
+                                        (key & 15)) * slot_stride + head_off + chunk * 8;
           lds_dma16(src, lds_base + dst);
         } else {  // past the item's keys: zero, never stale LDS contents
           *reinterpret_cast<uint4*>(&lds[dst + lane * 16]) = make_uint4(0, 0, 0, 0);
@@ -353,13 +359,12 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 
   // ---- prologue: K(0), V(0), K(1) by DMA; scores of tile 0 ----
   f32x16 sacc[2];
-  int32_t pg_v[IPW], pg_k[IPW];
-  pages(0, pg_v);
+  int32_t pg_v = pages(0);
   issue(kp, 0, 0, pg_v);
   issue(vp, 0, 2, pg_v);
-  pages(1, pg_v);
+  pg_v = pages(1);
   if (n_tiles > 1) issue(kp, 1, 1, pg_v);
-  pages(2, pg_k);
+  int32_t pg_k = pages(2);
   wait_dma();
   __syncthreads();
   scores(sacc, 0);
@@ -400,9 +405,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     if constexpr (kHasNext) {
       if (j + 2 < n_tiles) issue(kp, j + 2, P, pg_k);
       issue(vp, j + 1, 3 - P, pg_v);
-#pragma unroll
-      for (int r = 0; r < IPW; ++r) pg_v[r] = pg_k[r];
-      pages(j + 3, pg_k);
+      pg_v = pg_k;
+      pg_k = pages(j + 3);
     }
     const int t0 = it.kv_begin + 64 * j;
     if (t0 + 63 > wave_pos0) {  // wave-uniform: some key is past some row
