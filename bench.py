@@ -102,23 +102,24 @@ def _oracle_threads() -> int:
     return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
 
 
-def cpu_baseline_prefill(b):
-    """The float64 CPU oracle on request 0 of the prefill batch (4096 tokens,
-    all 32 q heads): 1/8 of the prefill workload, same inputs."""
+def cpu_baseline_prefill(b, n=2):
+    """The float64 CPU oracle on the first ``n`` requests of the prefill batch
+    (4096 tokens each, all 32 q heads): n/8 of the prefill workload, same
+    inputs."""
     import oracle
     import workloads as W
-    q, kp, vp, qo_ip, kv_ip, pt, _ = W.host_subset(b, [0])
+    q, kp, vp, qo_ip, kv_ip, pt, _ = W.host_subset(b, list(range(n)))
     t = time.perf_counter()
     oracle.attention_paged(q, kp, vp, qo_ip, kv_ip, pt, b.num_kv_heads, b.sm_scale)
     dt = time.perf_counter() - t
     fl = prefill_flops(np.diff(qo_ip), np.diff(kv_ip), b.num_qo_heads, b.head_dim)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": _oracle_threads(), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "prefill request 0 of 8 (4096 tokens, all 32 q heads): 1/8 of "
-                      "the prefill workload, same seeded inputs"}
+            "sample": f"prefill requests 0..{n - 1} of 8 (4096 tokens each, all 32 q "
+                      f"heads): {n}/8 of the prefill workload, same seeded inputs"}
 
 
-def cpu_baseline_decode(b, n=8):
+def cpu_baseline_decode(b, n=16):
     """The float64 CPU oracle on the first ``n`` decode requests."""
     import oracle
     import workloads as W
