@@ -17,7 +17,9 @@ forms, a hand example, a dense library computation and exact invariances, and
 ``tests/test_oracle_mutations.py`` shows that planted mistakes fail those pins.
 """
 from .attention import (attend, attention_paged, decode_paged, gather_request_kv,
-                        kv_head_of, merge_states, page_offsets, query_position)
+                        kv_head_of, latent_values, merge_states, mla_attention_paged,
+                        page_offsets, query_position)
 
 __all__ = ["attend", "attention_paged", "decode_paged", "gather_request_kv",
-           "kv_head_of", "merge_states", "page_offsets", "query_position"]
+           "kv_head_of", "latent_values", "merge_states", "mla_attention_paged",
+           "page_offsets", "query_position"]

@@ -103,16 +103,17 @@ def attention_paged(q, k_pool, v_pool, qo_indptr, kv_indptr, page_table,
                     row_block: int = 1024):
     """Causal attention of every (or of the selected) query rows of a batch.
 
-    ``q [sum qo, Hq, D]``; pools ``[num_pages, P, Hkv, D]``; indptrs ``[B+1]``.
-    ``rows`` selects global query rows (indices into ``q``'s first axis); rows
-    not selected are left NaN. Returns ``out [sum qo, Hq, D]`` and
-    ``lse [sum qo, Hq]`` in float64.
+    ``q [sum qo, Hq, Dk]``; ``k_pool [num_pages, P, Hkv, Dk]``, ``v_pool
+    [num_pages, P, Hkv, Dv]``; indptrs ``[B+1]``. ``rows`` selects global
+    query rows (indices into ``q``'s first axis); rows not selected are left
+    NaN. Returns ``out [sum qo, Hq, Dv]`` and ``lse [sum qo, Hq]`` in float64.
     """
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
     kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
     page_table = np.asarray(page_table, dtype=np.int64)
     q = _f64(q)
-    n_q, Hq, D = q.shape
+    n_q, Hq, _ = q.shape
+    D = v_pool.shape[3]          # output width: the value dim (may differ from q's)
     group = Hq // num_kv_heads
     P = k_pool.shape[1]
     B = len(qo_indptr) - 1
@@ -186,3 +187,28 @@ def merge_states(v, s, state_indptr):
             out[i, h] = (w[:, None] * v[lo:hi, h][live]).sum(axis=0) / w.sum()
             lse[i, h] = M + math.log(w.sum())
     return out, lse
+
+
+def latent_values(kv_pool, v_dim: int):
+    """Values of latent (absorbed multi-head latent) attention: the first
+    ``v_dim`` dims of every cached latent row (the rest is the rope part,
+    which only enters the scores)."""
+    return kv_pool[..., :v_dim]
+
+
+def mla_attention_paged(q, kv_pool, qo_indptr, kv_indptr, page_table, sm_scale: float,
+                        v_dim: int, rows: Optional[Sequence[int]] = None):
+    """Causal attention over a paged latent cache: every q head scores against
+    the full latent row (``Dk`` dims: latent + rope) of one shared cache head
+    and averages its first ``v_dim`` dims. The pages name this MLA wrapper as
+    the one path without a deterministic mode (sglang PR #43612, commit
+    message and Summary); the reading here is the absorbed form, with the
+    same causal alignment and page layout as the other calls.
+
+    ``q [sum qo, Hq, Dk]``; ``kv_pool [num_pages, P, Dk]`` or
+    ``[num_pages, P, 1, Dk]``. Returns ``out [sum qo, Hq, v_dim]`` and
+    ``lse [sum qo, Hq]`` (float64).
+    """
+    k_pool = kv_pool if kv_pool.ndim == 4 else kv_pool[:, :, None, :]
+    return attention_paged(q, k_pool, latent_values(k_pool, v_dim), qo_indptr, kv_indptr,
+                           page_table, 1, sm_scale, rows=rows)

@@ -9,7 +9,9 @@ Each ``pin_*`` raises ``AssertionError`` when the oracle disagrees with:
   never-paged copies of K and V,
 * exact invariances (chunked rows equal unchunked rows; decode equals the last
   prefill row; relocating pages changes nothing; V + c gives out + c; GQA
-  equals MHA with repeated kv heads).
+  equals MHA with repeated kv heads),
+* for latent (MLA) attention: one key, identical keys, and a dense library
+  computation over the contiguous latent rows.
 
 The pins reach the oracle through the module ``oracle.attention`` so that
 ``test_oracle_mutations.py`` can swap one of its functions for a copy with a
@@ -284,9 +286,79 @@ def pin_gqa_is_repeated_mha():
     _close(l1, l2, 0.0, "GQA vs repeated MHA: lse")
 
 
+# ------------------------------------------------------------- latent (MLA) --
+
+def _run_mla(b: W.PagedBatch, rows=None):
+    return A.mla_attention_paged(b.q, b.k_pool, b.qo_indptr, b.kv_indptr, b.page_table,
+                                 b.sm_scale, W.MLA_DV, rows=rows)
+
+
+def pin_mla_one_key():
+    """One visible key: out is the first 512 dims of that latent row, lse its
+    scaled score over all 576 dims."""
+    b = W.make_mla_batch([W.Request(1, 1, 41), W.Request(2, 2, 42)], num_qo_heads=4,
+                         num_pages=8, batch_seed=9, keep_seq=True)
+    out, lse = _run_mla(b)
+    for r, row in ((0, 0), (1, 1)):    # request 1's first query sees its key 0 only
+        kv0 = _f64(b.k_seq[r][0, 0])
+        g = int(b.qo_indptr[r])
+        _close(out[g, :, :], np.broadcast_to(kv0[:W.MLA_DV], (4, W.MLA_DV)), TOL,
+               "MLA one key: out")
+        q = _f64(b.q[g])
+        _close(lse[g], b.sm_scale * (q @ kv0), TOL, "MLA one key: lse")
+
+
+def pin_mla_identical_keys():
+    """All latent rows equal: out is that row's first 512 dims and lse =
+    s + ln(number of visible keys)."""
+    kv_len, qo = 37, 5
+    row = torch.randn(W.MLA_DK, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    kv = row.expand(kv_len, 1, W.MLA_DK).clone()
+    q = torch.randn(qo, 2, W.MLA_DK, generator=torch.Generator().manual_seed(6))
+    b = W.assemble_batch([qo], [kv_len], [q], [kv], [kv], num_pages=8, batch_seed=3,
+                         sm_scale=1.0 / math.sqrt(192.0))
+    b.v_pool = b.k_pool[..., :W.MLA_DV]
+    out, lse = _run_mla(b)
+    r64 = _f64(row)
+    qd = _f64(b.q)
+    for i in range(qo):
+        n_vis = kv_len - qo + i + 1
+        _close(out[i], np.broadcast_to(r64[:W.MLA_DV], (2, W.MLA_DV)), TOL,
+               "MLA identical keys: out")
+        _close(lse[i], b.sm_scale * (qd[i] @ r64) + math.log(n_vis), TOL,
+               "MLA identical keys: lse")
+
+
+def pin_mla_dense():
+    """Dense float64 library attention over the contiguous latent rows (no page
+    reads): every q head against the one shared row, values its first 512
+    dims, explicit bottom-right causal mask."""
+    reqs = [W.Request(1, 40, 51), W.Request(6, 23, 52), W.Request(17, 17, 53),
+            W.Request(0, 9, 54)]
+    b = W.make_mla_batch(reqs, num_qo_heads=8, num_pages=32, batch_seed=11, keep_seq=True)
+    out, lse = _run_mla(b)
+    for r in range(b.batch):
+        qo, kv = int(b.qo_lens()[r]), int(b.kv_lens()[r])
+        if qo == 0:
+            continue
+        q = b.q[b.qo_indptr[r]: b.qo_indptr[r + 1]].double().transpose(0, 1)  # [H, qo, Dk]
+        k = b.k_seq[r][:, 0].double()                                            # [kv, Dk]
+        i = torch.arange(qo)[:, None]
+        j = torch.arange(kv)[None, :]
+        mask = j <= (kv - qo) + i
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q, k.expand(8, kv, W.MLA_DK), k[:, :W.MLA_DV].expand(8, kv, W.MLA_DV),
+            attn_mask=mask, scale=b.sm_scale)
+        s = (b.sm_scale * (q @ k.T)).masked_fill(~mask, float("-inf"))
+        g0 = int(b.qo_indptr[r])
+        _close(out[g0: g0 + qo], o.transpose(0, 1).numpy(), 1e-12, "MLA dense: out")
+        _close(lse[g0: g0 + qo], torch.logsumexp(s, dim=-1).T.numpy(), 1e-12, "MLA dense: lse")
+
+
 ALL_PINS = [pin_one_key, pin_identical_keys, pin_hand_example, pin_dense_library,
             pin_causal_library, pin_merge, pin_chunk_and_decode_consistency,
-            pin_page_relocation, pin_value_shift, pin_gqa_is_repeated_mha]
+            pin_page_relocation, pin_value_shift, pin_gqa_is_repeated_mha,
+            pin_mla_one_key, pin_mla_identical_keys, pin_mla_dense]
 
 
 def failing_pins():

@@ -93,6 +93,8 @@ MUTATIONS = {
     "merge_weight_sign": ("merge_states", _merge_variant(sign=-1.0)),
     "merge_no_division": ("merge_states", _merge_variant(divide=False)),
     "merge_lse_drops_max": ("merge_states", _merge_variant(add_max=False)),
+    "mla_values_from_rope_end": ("latent_values", lambda kv, v_dim: kv[..., -v_dim:]),
+    "mla_values_skip_first_dim": ("latent_values", lambda kv, v_dim: kv[..., 1:v_dim + 1]),
 }
 
 

@@ -206,6 +206,42 @@ def assemble_batch(qo_lens, kv_lens, q_list, k_list, v_list, *, num_pages: int,
                       k_pool, v_pool, [], k_seq, v_seq)
 
 
+# Latent cache of multi-head latent attention (absorbed form): each token keeps
+# one row of MLA_DK = 512 latent + 64 rope dims, shared by every q head; the
+# values are its first MLA_DV dims.
+MLA_DK = 576
+MLA_DV = 512
+
+
+def make_mla_batch(requests: Sequence[Request], *, num_qo_heads: int, num_pages: int,
+                   batch_seed: int, sm_scale: Optional[float] = None, device="cpu",
+                   keep_seq: bool = False,
+                   page_table: Optional[np.ndarray] = None) -> PagedBatch:
+    """Latent-cache batch: per request, ``kv_len`` latent rows ``[kv_len, 1,
+    MLA_DK]`` and then ``qo_len`` queries ``[qo_len, Hq, MLA_DK]`` drawn from a
+    generator seeded with the request's seed. ``k_pool`` is the latent pool
+    ``[num_pages, 16, 1, MLA_DK]``; ``v_pool`` is a view of its first MLA_DV
+    dims. The default scale is ``1 / sqrt(192)`` (the per-head q.k width of the
+    un-absorbed form, 128 + 64)."""
+    reqs = list(requests)
+    kvs, qs = [], []
+    for r in reqs:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(r.seed))
+        kvs.append(_normal_bf16((r.kv_len, 1, MLA_DK), gen, device))
+        qs.append(_normal_bf16((r.qo_len, num_qo_heads, MLA_DK), gen, device))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(192.0)
+    b = assemble_batch([r.qo_len for r in reqs], [r.kv_len for r in reqs], qs, kvs, kvs,
+                       num_pages=num_pages, batch_seed=batch_seed, sm_scale=sm_scale,
+                       device=device, keep_seq=keep_seq, page_table=page_table)
+    b.v_pool = b.k_pool[..., :MLA_DV]
+    if keep_seq:
+        b.v_seq = [k[..., :MLA_DV] for k in b.k_seq]
+    b.requests = reqs
+    return b
+
+
 @dataclass
 class Sequence1:
     """One long request stored once in a pool, viewed as chunked calls.
