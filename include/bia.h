@@ -87,6 +87,12 @@ typedef enum bia_mode {
  * kv_len - qo_len is not a multiple of bia_prefill_chunk_align() tokens (the
  * startup rejection of a misaligned chunk size, sglang PR #43612, Summary). */
 #define BIA_PLAN_STRICT_CHUNK_ALIGN 0x1u
+/* Latent (MLA) plan: num_kv_heads 1 and head_dim 576 (512 latent + 64 rope
+ * dims of the one cached row per token), values the first 512 of them; run it
+ * with bia_mla_prefill_paged / bia_mla_decode_paged. */
+#define BIA_PLAN_MLA 0x2u
+#define BIA_MLA_QK_DIM 576
+#define BIA_MLA_V_DIM 512
 
 typedef struct bia_plan bia_plan; /* opaque, library-owned */
 
@@ -106,7 +112,9 @@ typedef struct bia_plan bia_plan; /* opaque, library-owned */
  *       BIA_DECODE_SPLIT for the pages' setting). Keys of request r are cut
  *       into partitions [k * split_size, (k + 1) * split_size), anchored at
  *       key 0 of the request.
- *   flags: 0 or BIA_PLAN_STRICT_CHUNK_ALIGN.
+ *   flags: 0, BIA_PLAN_STRICT_CHUNK_ALIGN, BIA_PLAN_MLA or both. An MLA plan
+ *       takes num_kv_heads 1, head_dim BIA_MLA_QK_DIM and num_qo_heads 8, 16,
+ *       32, 64 or 128 (the one cached head is shared by every q head).
  * On success *out_plan receives a plan to free with bia_plan_destroy. The
  * arrays are not retained. batch == 0 gives an empty plan whose runs do
  * nothing.
@@ -155,6 +163,36 @@ bia_status bia_decode_paged(const bia_plan* plan, const void* q,
                             const int32_t* page_table_dev, float sm_scale,
                             void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Latent (MLA) attention over a paged latent cache, absorbed form: the MLA
+ * decode path that the pages name as lacking a deterministic mode (sglang PR
+ * #43612, Summary), given the same fixed-split, fixed-order treatment as the
+ * calls above (sglang PR #10417, Modifications). Every q head scores its 576
+ * dims against the one cached 576-dim row of each key and averages the first
+ * 512 dims of those rows:
+ *   out[t][h] = sum_j softmax_j(sm_scale * q[t][h] . kv[j]) kv[j][0:512]
+ * over the keys j <= the token's position (causal; decode: all kv_len keys).
+ *   plan: made with BIA_PLAN_MLA, of the call's mode;
+ *   q: device bf16 [sum qo_len][Hq][576]; kv_pool: device bf16
+ *   [num_pages][16][576]; out: device bf16 [sum qo_len][Hq][512]; lse: device
+ *   fp32 [sum qo_len][Hq] or NULL; page_table_dev, workspace: as for
+ *   bia_prefill_paged.
+ * A plan without BIA_PLAN_MLA is rejected (BIA_ERR_INVALID_ARG), and so is an
+ * MLA plan passed to bia_prefill_paged / bia_decode_paged /
+ * bia_append_paged_kv. Output bits of a request depend only on its q, its
+ * cached rows, qo_len, kv_len, split_size, Hq and sm_scale.
+ */
+bia_status bia_mla_prefill_paged(const bia_plan* plan, const void* q,
+                                 const void* kv_pool, const int32_t* page_table_dev,
+                                 float sm_scale, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+bia_status bia_mla_decode_paged(const bia_plan* plan, const void* q,
+                                const void* kv_pool, const int32_t* page_table_dev,
+                                float sm_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * Merge partial attention states in a fixed order: row i folds states

@@ -24,6 +24,9 @@ BIA_Q_TILE_ROWS = 128
 BIA_KV_TILE = 64
 BIA_PAGE_SIZE = 16
 BIA_PLAN_STRICT_CHUNK_ALIGN = 0x1
+BIA_PLAN_MLA = 0x2
+BIA_MLA_QK_DIM = 576
+BIA_MLA_V_DIM = 512
 
 _STATUS = {0: "BIA_OK", 1: "BIA_ERR_INVALID_ARG", 2: "BIA_ERR_SHAPE",
            3: "BIA_ERR_PAGE_RANGE", 4: "BIA_ERR_WORKSPACE", 5: "BIA_ERR_UNSUPPORTED",
@@ -69,6 +72,11 @@ def load_library():
     lib.bia_prefill_paged.argtypes = run_args
     lib.bia_decode_paged.restype = i32
     lib.bia_decode_paged.argtypes = run_args
+    mla_args = [vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.bia_mla_prefill_paged.restype = i32
+    lib.bia_mla_prefill_paged.argtypes = mla_args
+    lib.bia_mla_decode_paged.restype = i32
+    lib.bia_mla_decode_paged.argtypes = mla_args
     lib.bia_append_paged_kv.restype = i32
     lib.bia_append_paged_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.bia_merge_states.restype = i32
@@ -121,8 +129,10 @@ class Plan:
     only after every run enqueued with it has completed."""
 
     def __init__(self, handle, mode, batch, num_qo_heads, num_kv_heads, head_dim,
-                 num_pages, total_q, total_pages, split_size):
+                 num_pages, total_q, total_pages, split_size, flags=0):
         self._h = handle
+        self.flags = flags
+        self.mla = bool(flags & BIA_PLAN_MLA)
         self.mode = mode
         self.batch = batch
         self.num_qo_heads = num_qo_heads
@@ -187,7 +197,7 @@ def bia_plan_create(mode, qo_indptr, kv_indptr, page_table, *, num_qo_heads,
     kv_lens = np.diff(kv.astype(np.int64))
     total_pages = int(((kv_lens + page_size - 1) // page_size).sum()) if batch else 0
     return Plan(handle.value, int(mode), batch, num_qo_heads, num_kv_heads, head_dim,
-                num_pages, int(qo[-1]) if batch else 0, total_pages, split_size)
+                num_pages, int(qo[-1]) if batch else 0, total_pages, split_size, int(flags))
 
 
 def bia_plan_workspace_bytes(plan: Plan) -> int:
@@ -240,6 +250,8 @@ def _run(fn, plan: Plan, mode, q, k_pool, v_pool, page_table_dev, sm_scale, out,
     torch = _torch()
     if plan.mode != mode:
         raise BiaError(1, "plan was made for the other mode")
+    if plan.mla:
+        raise BiaError(1, "an MLA plan runs through bia_mla_*_paged")
     dev = q.device if isinstance(q, torch.Tensor) else None
     bf16 = torch.bfloat16
     Hq, Hkv, D = plan.num_qo_heads, plan.num_kv_heads, plan.head_dim
@@ -270,6 +282,46 @@ def bia_decode_paged(plan: Plan, q, k_pool, v_pool, page_table_dev, sm_scale, ou
     """Paged decode, one query token per request (see ``bia_decode_paged``)."""
     _run(load_library().bia_decode_paged, plan, BIA_MODE_DECODE, q, k_pool, v_pool,
          page_table_dev, sm_scale, out, lse, workspace, stream)
+
+
+def _run_mla(fn, plan: Plan, mode, q, kv_pool, page_table_dev, sm_scale, out, lse,
+             workspace, stream):
+    torch = _torch()
+    if plan.mode != mode:
+        raise BiaError(1, "plan was made for the other mode")
+    if not plan.mla:
+        raise BiaError(1, "plan was not made with BIA_PLAN_MLA")
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    bf16 = torch.bfloat16
+    Hq = plan.num_qo_heads
+    qp = _dev_ptr(q, "q", bf16, (plan.total_q, Hq, BIA_MLA_QK_DIM))
+    kvp = _dev_ptr(kv_pool, "kv_pool", bf16, (plan.num_pages, BIA_PAGE_SIZE, BIA_MLA_QK_DIM),
+                   device=dev)
+    ptp = _dev_ptr(page_table_dev, "page_table_dev", torch.int32,
+                   min_numel=plan.total_pages, device=dev)
+    op = _dev_ptr(out, "out", bf16, (plan.total_q, Hq, BIA_MLA_V_DIM), device=dev)
+    lp = None if lse is None else _dev_ptr(lse, "lse", torch.float32,
+                                          (plan.total_q, Hq), device=dev)
+    wp = _dev_ptr(workspace, "workspace", torch.uint8, min_numel=plan.workspace_bytes,
+                  device=dev)
+    _check(fn(ctypes.c_void_p(plan.handle), qp, kvp, ptp, float(sm_scale), op, lp, wp,
+              workspace.numel(), _stream_handle(stream, q.device)))
+
+
+def bia_mla_prefill_paged(plan: Plan, q, kv_pool, page_table_dev, sm_scale, out, lse,
+                          workspace, stream=None):
+    """Causal latent (MLA) prefill over a paged latent cache (see
+    ``bia_mla_prefill_paged`` in bia.h)."""
+    _run_mla(load_library().bia_mla_prefill_paged, plan, BIA_MODE_PREFILL, q, kv_pool,
+             page_table_dev, sm_scale, out, lse, workspace, stream)
+
+
+def bia_mla_decode_paged(plan: Plan, q, kv_pool, page_table_dev, sm_scale, out, lse,
+                         workspace, stream=None):
+    """Latent (MLA) decode, one query token per request (see
+    ``bia_mla_decode_paged``)."""
+    _run_mla(load_library().bia_mla_decode_paged, plan, BIA_MODE_DECODE, q, kv_pool,
+             page_table_dev, sm_scale, out, lse, workspace, stream)
 
 
 def bia_append_paged_kv(plan: Plan, k_new, v_new, page_table_dev, k_pool, v_pool,

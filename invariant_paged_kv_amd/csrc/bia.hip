@@ -866,6 +866,248 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------
+// Latent (MLA) attention, absorbed form: every q head scores against the one
+// cached latent row per token (576 bf16: 512 latent + 64 rope dims) and
+// averages its first 512 dims (the pages name this MLA path as the one with
+// no deterministic mode, sglang PR #43612, commit message and Summary).
+//
+// One workgroup = one WorkItem = 64 q rows (64 / hb tokens x hb heads of one
+// head block, hb = min(Hq, 64); the plan's "kv head" is the head block) over
+// one split-KV partition; 4 waves x 16 rows. Per 32-key tile, staged in LDS
+// by all threads (global loads of tile j+1 in flight while tile j computes;
+// rows padded to 1168 bytes, which keeps both the K-operand reads and the
+// transposing V reads on distinct banks):
+//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys as M, the wave's 16 rows
+//   as N, 576 dims as 18 k-steps; layout checked on the GPU with an exact
+//   integer probe: A[m][k]: m = l % 16, k = 8 (l / 16) + e; B[k][n]:
+//   n = l % 16, same k; D[m][n]: n = l % 16, m = 4 (l / 16) + v), so row n's
+//   32 scores sit in lanes n, n + 16, n + 32, n + 48;
+//   online softmax per row (lazy max, exp2 with the scale folded in, fp32
+//   row sum), max and sums combined over the four lanes with symmetric
+//   permlane swaps;
+//   O^T += V^T P^T over the wave's 16 rows and all 512 value dims (32 MFMAs):
+//   the probabilities stay in registers as the B operand, in the key order
+//   the score MFMA left them (slot 8 g + e is key 4 g + e for e < 4 and
+//   16 + 4 g + e - 4 otherwise), and V^T is read in that order with
+//   ds_read_b64_tr_b16.
+// The same invariance rules hold as for the other kernels: tiles anchored at
+// the partition start, masked tiles exact no-ops, per-row arithmetic
+// independent of the tile holding the row.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMlaDk = BIA_MLA_QK_DIM;
+constexpr int kMlaDv = BIA_MLA_V_DIM;
+constexpr int kMlaKeys = 32;                              // keys per tile
+constexpr int kMlaRowBytes = kMlaDk * 2 + 16;             // padded LDS row
+constexpr int kMlaTileBytes = kMlaKeys * kMlaRowBytes;    // 37376
+constexpr int kMlaChunks = kMlaDk / 8;                    // 16-byte pieces per row
+constexpr int kMlaLoads = kMlaKeys * kMlaChunks / kThreads;  // per thread per tile
+static_assert(kMlaKeys * kMlaChunks % kThreads == 0, "tile loads split evenly");
+
+// max and sum over the lanes n, n ^ 16, n ^ 32, n ^ 48 (symmetric: every lane
+// of the four gets the same bits)
+__device__ __forceinline__ float quad_max(float x) {
+  float a, b;
+  lane_swap(0, x, a, b);
+  x = fmaxf(a, b);
+  lane_swap(1, x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  float a, b;
+  lane_swap(0, x, a, b);
+  x = a + b;
+  lane_swap(1, x, a, b);
+  return a + b;
+}
+
+__global__ void __launch_bounds__(kThreads, 1)
+mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
+           const uint16_t* __restrict__ kvp, const int32_t* __restrict__ page_table,
+           float scale_log2, int num_qo_heads, int hb_shift, int split,
+           uint16_t* __restrict__ out, float* __restrict__ lse_out,
+           float* __restrict__ o_part, float* __restrict__ lse_part) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMlaTileBytes];
+  const WorkItem it = items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4;   // 16-lane group
+  const int n16 = lane & 15;  // the lane's row among the wave's 16 (and its M index)
+  const int hb = 1 << hb_shift;
+  const int x = wave * 16 + n16;  // row of the 64-row tile
+  const int tok = x >> hb_shift;
+  const int hq = it.kv_head * hb + (x & (hb - 1));
+  const bool row_valid = tok < it.n_tok;
+  const int pos = row_valid ? it.pos0 + tok : -1;
+  const int wave_pos0 = it.pos0 + ((wave * 16) >> hb_shift);
+  const int64_t row_idx = static_cast<int64_t>(it.q_row0 + tok) * num_qo_heads + hq;
+
+  // Q^T fragments (B operand): row n16, dims 32 s + 8 g4 .. + 7
+  bf16x8 qf[kMlaDk / 32];
+#pragma unroll
+  for (int s = 0; s < kMlaDk / 32; ++s) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row_valid)
+      w = *reinterpret_cast<const uint4*>(q + row_idx * kMlaDk + 32 * s + 8 * g4);
+    qf[s] = __builtin_bit_cast(bf16x8, w);
+  }
+
+  const int last = it.pos0 + it.n_tok - 1;
+  const int kv_end = min(it.kv_begin + split, last + 1);
+  const int n_tiles = (kv_end - it.kv_begin + kMlaKeys - 1) / kMlaKeys;
+  const int32_t* pt = page_table + it.page_off;
+  const int last_page = (kv_end - 1) >> 4;
+
+  // Tile loads: thread t moves pieces i = t + 256 u: key row i / 72, piece
+  // i % 72. A tile's 32 keys are two pages; their ids come from one vector
+  // load made a tile ahead (lane l holds page l % 2).
+  uint4 stage[kMlaLoads];
+  auto page_pair = [&](int t) -> int32_t {
+    return pt[min(((it.kv_begin + kMlaKeys * t) >> 4) + (lane & 1), last_page)];
+  };
+  auto load_tile = [&](int t, int32_t pgv) {
+    const int t0 = it.kv_begin + kMlaKeys * t;
+    const int32_t pa = __builtin_amdgcn_readlane(pgv, 0);
+    const int32_t pb = __builtin_amdgcn_readlane(pgv, 1);
+#pragma unroll
+    for (int u = 0; u < kMlaLoads; ++u) {
+      const int i = tid + kThreads * u;
+      const int row = i / kMlaChunks;
+      const int piece = i % kMlaChunks;
+      const int key = t0 + row;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (key < kv_end) {  // past the item's keys: zero, never stale LDS contents
+        const int64_t page = row < 16 ? pa : pb;
+        w = *reinterpret_cast<const uint4*>(kvp + (page * 16 + (key & 15)) * kMlaDk + piece * 8);
+      }
+      stage[u] = w;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kMlaLoads; ++u) {
+      const int i = tid + kThreads * u;
+      *reinterpret_cast<uint4*>(&lds[buf * kMlaTileBytes + (i / kMlaChunks) * kMlaRowBytes +
+                                     (i % kMlaChunks) * 16]) = stage[u];
+    }
+  };
+
+  float m = kNegInf;   // running max (base-2 scaled), stale by < kLazyMax
+  float lsum = 0.0f;   // this lane's share of the row's running sum
+  f32x4 o[kMlaDv / 16];
+#pragma unroll
+  for (int b = 0; b < kMlaDv / 16; ++b) o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int j, int buf) {
+    const uint8_t* base = &lds[buf * kMlaTileBytes];
+    // ---- scores: S^T for keys 16 kb + m (m = n16) x the wave's 16 rows ----
+    f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    const uint8_t* kb0 = base + n16 * kMlaRowBytes + g4 * 16;
+#pragma unroll
+    for (int s = 0; s < kMlaDk / 32; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kb0 + kb * 16 * kMlaRowBytes + s * 64);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[s],
+                                                         sc[kb], 0, 0, 0);
+      }
+    }
+    const int t0 = it.kv_begin + kMlaKeys * j;
+    if (t0 + kMlaKeys - 1 > wave_pos0) {  // wave-uniform: some key is past some row
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sc[kb][v] = (t0 + 16 * kb + 4 * g4 + v <= pos) ? sc[kb][v] : kNegInf;
+    }
+    // ---- online softmax of the row ----
+    float mx = sc[0][0];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) mx = fmaxf(mx, sc[0][v]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[1][v]);
+    const float mt = quad_max(mx) * scale_log2;
+    const bool raise = mt > m + kLazyMax;  // true on the first tile with a visible key
+    const float m_new = raise ? mt : m;
+    const float alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p[kb][v] = fast_exp2(__builtin_fmaf(sc[kb][v], scale_log2, neg_m));
+        psum += p[kb][v];
+      }
+    const uint4 pw = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
+    if (__any(raise)) {  // lanes that did not raise have alpha == 1 exactly
+      lsum *= alpha;
+#pragma unroll
+      for (int b = 0; b < kMlaDv / 16; ++b) o[b] *= alpha;
+    }
+    lsum += psum;
+    m = m_new;
+    // ---- O^T += V^T P^T: 32 blocks of 16 value dims ----
+    const uint8_t* v0 = base + (4 * g4 + (n16 >> 2)) * kMlaRowBytes + (n16 & 3) * 8;
+    const uint8_t* v1 = v0 + 16 * kMlaRowBytes;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b) {
+      const uint2 lo = lds_read_tr16(v0 + b * 32);
+      const uint2 hi = lds_read_tr16(v1 + b * 32);
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)),
+          __builtin_bit_cast(bf16x8, pw), o[b], 0, 0, 0);
+    }
+  };
+
+  int32_t pgv = page_pair(0);
+  load_tile(0, pgv);
+  store_tile(0);
+  pgv = page_pair(1);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    if (j + 1 < n_tiles) {
+      load_tile(j + 1, pgv);
+      pgv = page_pair(j + 2);
+    }
+    compute(j, j & 1);
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);  // the buffer tile j-1 used
+    __syncthreads();
+  }
+
+  // ---- this partition's state for the row: o = O / l, lse = m + log l ----
+  const float l_row = quad_sum(lsum);
+  if (!row_valid) return;
+  float lse_nat = kNegInf;
+  float inv = 0.0f;
+  if (l_row > 0.0f) {
+    inv = 1.0f / l_row;
+    lse_nat = (m + fast_log2(l_row)) * kLn2;
+  }
+  if (it.state < 0) {
+    uint16_t* orow = out + row_idx * kMlaDv;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b) {
+      *reinterpret_cast<uint2*>(orow + 16 * b + 4 * g4) =
+          make_uint2(pack_bf16x2(o[b][0] * inv, o[b][1] * inv),
+                     pack_bf16x2(o[b][2] * inv, o[b][3] * inv));
+    }
+    if (lse_out != nullptr && g4 == 0) lse_out[row_idx] = lse_nat;
+  } else {
+    const int64_t st = static_cast<int64_t>(it.state) + x;
+    float* orow = o_part + st * kMlaDv;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b)
+      *reinterpret_cast<float4*>(orow + 16 * b + 4 * g4) =
+          make_float4(o[b][0] * inv, o[b][1] * inv, o[b][2] * inv, o[b][3] * inv);
+    if (g4 == 0) lse_part[st] = lse_nat;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of a tile's partitions (prefill rows spanning several partitions,
 // decode requests longer than one partition): row x of MergeItem mi folds
 // slots state0 + k * stride + x, k ascending, with fold_state. D/4 threads
@@ -1140,12 +1382,15 @@ bia_status ensure_pinned(const bia_plan* plan) {
 
 int log2_exact(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
-bia_status check_run(const bia_plan* plan, bia_mode mode, const void* q, const void* k_pool,
+bia_status check_run(const bia_plan* plan, bia_mode mode, bool mla, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* page_table_dev, float sm_scale,
                      const void* out, const void* workspace, size_t workspace_bytes) {
   if (plan == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->d.mode != mode)
     return bia::fail(BIA_ERR_INVALID_ARG, "plan was made for the other mode");
+  if (plan->d.mla != mla)
+    return bia::fail(BIA_ERR_INVALID_ARG, mla ? "plan was not made with BIA_PLAN_MLA"
+                                              : "an MLA plan runs through bia_mla_*_paged");
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return bia::fail(BIA_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   if (plan->d.items.empty()) return BIA_OK;
@@ -1231,7 +1476,7 @@ extern "C" bia_status bia_prefill_paged(const bia_plan* plan, const void* q, con
                                         const void* v_pool, const int32_t* page_table_dev,
                                         float sm_scale, void* out, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream_handle) {
-  bia_status st = check_run(plan, BIA_MODE_PREFILL, q, k_pool, v_pool, page_table_dev, sm_scale,
+  bia_status st = check_run(plan, BIA_MODE_PREFILL, false, q, k_pool, v_pool, page_table_dev, sm_scale,
                             out, workspace, workspace_bytes);
   if (st != BIA_OK || plan->d.items.empty()) return st;
   const bia::PlanData& d = plan->d;
@@ -1272,7 +1517,7 @@ extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, cons
                                        const void* v_pool, const int32_t* page_table_dev,
                                        float sm_scale, void* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream_handle) {
-  bia_status st = check_run(plan, BIA_MODE_DECODE, q, k_pool, v_pool, page_table_dev, sm_scale,
+  bia_status st = check_run(plan, BIA_MODE_DECODE, false, q, k_pool, v_pool, page_table_dev, sm_scale,
                             out, workspace, workspace_bytes);
   if (st != BIA_OK || plan->d.items.empty()) return st;
   const bia::PlanData& d = plan->d;
@@ -1300,6 +1545,58 @@ extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return BIA_OK;
+}
+
+namespace {
+
+bia_status run_mla(const bia_plan* plan, bia_mode mode, const void* q, const void* kv_pool,
+                   const int32_t* page_table_dev, float sm_scale, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream_handle) {
+  bia_status st = check_run(plan, mode, true, q, kv_pool, kv_pool, page_table_dev, sm_scale, out,
+                            workspace, workspace_bytes);
+  if (st != BIA_OK || plan->d.items.empty()) return st;
+  const bia::PlanData& d = plan->d;
+  hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+  st = upload(plan, workspace, stream);
+  if (st != BIA_OK) return st;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const ListLaunch L = plan_items(d, ws);
+  auto* o = static_cast<uint16_t*>(out);
+  int hb_shift = 0;
+  while ((1 << hb_shift) < d.group) ++hb_shift;
+  hipLaunchKernelGGL(mla_kernel, dim3(L.n), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const WorkItem*>(L.items), static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(kv_pool), page_table_dev, sm_scale * kLog2e,
+                     d.num_qo_heads, hb_shift, d.split, o, lse, L.o_part, L.lse_part);
+  if (!d.merges.empty()) {
+    const ListLaunch M = plan_merges(d, ws);
+    hipLaunchKernelGGL(merge_tiles_kernel<kMlaDv>, dim3(M.n), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const MergeItem*>(M.items), M.o_part, M.lse_part,
+                       M.num_qo_heads, hb_shift, o, lse);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "MLA launch");
+  return BIA_OK;
+}
+
+}  // namespace
+
+extern "C" bia_status bia_mla_prefill_paged(const bia_plan* plan, const void* q,
+                                            const void* kv_pool, const int32_t* page_table_dev,
+                                            float sm_scale, void* out, float* lse,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream_handle) {
+  return run_mla(plan, BIA_MODE_PREFILL, q, kv_pool, page_table_dev, sm_scale, out, lse,
+                 workspace, workspace_bytes, stream_handle);
+}
+
+extern "C" bia_status bia_mla_decode_paged(const bia_plan* plan, const void* q,
+                                           const void* kv_pool, const int32_t* page_table_dev,
+                                           float sm_scale, void* out, float* lse,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream_handle) {
+  return run_mla(plan, BIA_MODE_DECODE, q, kv_pool, page_table_dev, sm_scale, out, lse,
+                 workspace, workspace_bytes, stream_handle);
 }
 
 extern "C" bia_status bia_merge_states(const float* v, const float* s,
@@ -1339,6 +1636,8 @@ extern "C" bia_status bia_append_paged_kv(const bia_plan* plan, const void* k_ne
                                           size_t workspace_bytes, void* stream_handle) {
   if (plan == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "plan is NULL");
   const bia::PlanData& d = plan->d;
+  if (d.mla)
+    return bia::fail(BIA_ERR_UNSUPPORTED, "append into a latent (MLA) cache is not supported");
   if (d.appends.empty()) return BIA_OK;
   if (k_new == nullptr || v_new == nullptr || page_table_dev == nullptr || k_pool == nullptr ||
       v_pool == nullptr)

@@ -146,13 +146,35 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   if (batch < 0) return fail(BIA_ERR_INVALID_ARG, "batch %d < 0", batch);
   if (batch > 0 && (qo_indptr == nullptr || kv_indptr == nullptr))
     return fail(BIA_ERR_INVALID_ARG, "qo_indptr / kv_indptr is NULL");
-  const bia_status shape_st =
-      check_shape(num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, split_size);
-  if (shape_st != BIA_OK) return shape_st;
-  const int32_t group = num_qo_heads / num_kv_heads;
-
-  if ((flags & ~BIA_PLAN_STRICT_CHUNK_ALIGN) != 0)
+  if ((flags & ~(BIA_PLAN_STRICT_CHUNK_ALIGN | BIA_PLAN_MLA)) != 0)
     return fail(BIA_ERR_INVALID_ARG, "unknown plan flags 0x%x", flags);
+  const bool mla = (flags & BIA_PLAN_MLA) != 0;
+  int32_t group = 0;
+  if (mla) {
+    if (num_kv_heads != 1)
+      return fail(BIA_ERR_SHAPE, "an MLA plan has one cached head, got num_kv_heads %d",
+                  num_kv_heads);
+    if (head_dim != BIA_MLA_QK_DIM)
+      return fail(BIA_ERR_UNSUPPORTED, "MLA head_dim %d not supported (%d)", head_dim,
+                  BIA_MLA_QK_DIM);
+    if (num_qo_heads != 8 && num_qo_heads != 16 && num_qo_heads != 32 && num_qo_heads != 64 &&
+        num_qo_heads != 128)
+      return fail(BIA_ERR_UNSUPPORTED, "MLA num_qo_heads %d not supported (8 .. 128, a power "
+                  "of 2)", num_qo_heads);
+    if (page_size != kPageSize)
+      return fail(BIA_ERR_UNSUPPORTED, "page_size %d not supported (16)", page_size);
+    if (num_pages < 0) return fail(BIA_ERR_INVALID_ARG, "num_pages %d < 0", num_pages);
+    if (split_size <= 0 || split_size % kKvTile != 0)
+      return fail(BIA_ERR_INVALID_ARG,
+                  "split_size %d must be a positive multiple of the %d-key KV tile",
+                  split_size, kKvTile);
+    group = std::min(num_qo_heads, kMlaTileRows);  // q heads per head block
+  } else {
+    const bia_status shape_st =
+        check_shape(num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, split_size);
+    if (shape_st != BIA_OK) return shape_st;
+    group = num_qo_heads / num_kv_heads;
+  }
   int64_t total_pages = 0;
   if (batch > 0) {
     if (qo_indptr[0] != 0 || kv_indptr[0] != 0)
@@ -192,14 +214,16 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   d.mode = mode;
   d.batch = batch;
   d.num_qo_heads = num_qo_heads;
-  d.num_kv_heads = num_kv_heads;
+  d.num_kv_heads = mla ? num_qo_heads / group : num_kv_heads;
   d.head_dim = head_dim;
+  d.mla = mla;
+  d.v_dim = mla ? BIA_MLA_V_DIM : head_dim;
   d.page_size = page_size;
   d.num_pages = num_pages;
   d.split = split_size;
   d.flags = flags;
   d.group = group;
-  d.tile_tokens = kQTileRows / group;
+  d.tile_tokens = (mla ? kMlaTileRows : kQTileRows) / group;
   d.total_q = batch > 0 ? qo_indptr[batch] : 0;
   d.n_states = 0;
   bia_status st = BIA_OK;
@@ -217,7 +241,7 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   d.off_appends = d.off_merges + d.merges.size() * sizeof(MergeItem);
   d.blob_bytes = d.off_appends + d.appends.size() * sizeof(AppendItem);
   d.off_o = align_up(d.blob_bytes, kWsAlign);
-  d.off_lse = align_up(d.off_o + size_t(d.n_states) * head_dim * sizeof(float), kWsAlign);
+  d.off_lse = align_up(d.off_o + size_t(d.n_states) * d.v_dim * sizeof(float), kWsAlign);
   d.ws_bytes = d.n_states > 0 ? d.off_lse + size_t(d.n_states) * sizeof(float)
                               : align_up(d.blob_bytes, kWsAlign);
   d.blob.resize(d.blob_bytes);

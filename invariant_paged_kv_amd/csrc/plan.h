@@ -47,6 +47,7 @@ static_assert(sizeof(AppendItem) == 16, "append item is 4 int32");
 static_assert(sizeof(MergeItem) == 32, "merge item is 8 int32");
 
 constexpr int kQTileRows = BIA_Q_TILE_ROWS;
+constexpr int kMlaTileRows = 64;  // q rows of one latent-attention work item
 constexpr int kKvTile = BIA_KV_TILE;
 constexpr int kPageSize = BIA_PAGE_SIZE;
 constexpr size_t kWsAlign = 256;
@@ -56,6 +57,11 @@ struct PlanData {
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages;
   int32_t split, group, tile_tokens;
   uint32_t flags;
+  // Latent (MLA) plans: num_kv_heads counts head blocks of `group` q heads
+  // (all reading the one cached head), head_dim is the q.k width (576) and
+  // v_dim the output width (512); otherwise v_dim == head_dim.
+  bool mla;
+  int32_t v_dim;
   int64_t total_q;   // sum of qo_len: rows of q / out
   int64_t n_states;  // partial states written before the merge
   std::vector<WorkItem> items;

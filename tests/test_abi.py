@@ -38,7 +38,8 @@ def test_python_binding_has_every_entry_point():
                  "bia_prefill_chunk_align", "bia_last_error", "bia_append_paged_kv",
                  "bia_decode_graph_create", "bia_decode_graph_destroy",
                  "bia_decode_graph_workspace_bytes", "bia_decode_graph_run",
-                 "bia_decode_graph_read_flags"]:
+                 "bia_decode_graph_read_flags", "bia_mla_prefill_paged",
+                 "bia_mla_decode_paged"]:
         assert name in declared_functions()
         assert callable(getattr(bia, name)), name
 
@@ -71,7 +72,7 @@ def plan(mode=bia.BIA_MODE_PREFILL, qo=(0, 100, 400), kv=(0, 100, 400), pt=None,
     (dict(heads=dict(num_qo_heads=48, num_kv_heads=3, head_dim=64)), "BIA_ERR_UNSUPPORTED"),
     (dict(mode=bia.BIA_MODE_DECODE), "BIA_ERR_SHAPE"),            # decode needs qo_len 1
     (dict(mode=7), "BIA_ERR_INVALID_ARG"),
-    (dict(flags=0x2), "BIA_ERR_INVALID_ARG"),                     # unknown flag
+    (dict(flags=0x4), "BIA_ERR_INVALID_ARG"),                     # unknown flag
     # strict chunk alignment: starts at 0 and 128 pass, 100 is rejected
     (dict(qo=(0, 100, 400), kv=(0, 100, 400), flags=1), None),
     (dict(qo=(0, 172), kv=(0, 300), flags=1), None),
@@ -132,6 +133,87 @@ def test_run_rejects_wrong_mode_and_small_workspace():
                                float("nan"), dummy, None, dummy, p.workspace_bytes, None)
     assert st == 1
     p.close()
+
+
+# ------------------------------------------------------- latent (MLA) plans --
+
+MLA = dict(num_kv_heads=1, head_dim=bia.BIA_MLA_QK_DIM)
+
+
+@pytest.mark.parametrize("heads,status", [
+    (dict(num_qo_heads=16, **MLA), None),
+    (dict(num_qo_heads=128, **MLA), None),
+    (dict(num_qo_heads=8, **MLA), None),
+    (dict(num_qo_heads=12, **MLA), "BIA_ERR_UNSUPPORTED"),       # not a power of 2
+    (dict(num_qo_heads=256, **MLA), "BIA_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=16, num_kv_heads=2, head_dim=576), "BIA_ERR_SHAPE"),
+    (dict(num_qo_heads=16, num_kv_heads=1, head_dim=128), "BIA_ERR_UNSUPPORTED"),
+])
+def test_mla_plan_validation(heads, status):
+    kw = dict(heads=heads, flags=bia.BIA_PLAN_MLA)
+    if status is None:
+        plan(**kw).close()
+        return
+    with pytest.raises(bia.BiaError) as e:
+        plan(**kw)
+    assert str(e.value).startswith(status), str(e.value)
+
+
+def test_mla_plan_without_flag_rejects_576():
+    with pytest.raises(bia.BiaError) as e:
+        plan(heads=dict(num_qo_heads=16, **MLA))
+    assert str(e.value).startswith("BIA_ERR_UNSUPPORTED")
+
+
+@pytest.mark.parametrize("hq", [16, 128])
+def test_mla_items_cover_every_head_and_token(hq):
+    """Items of a latent plan: 64-row tiles of 64 / min(Hq, 64) tokens, one
+    per head block, so every (token, q head) row sits in exactly one tile of
+    each partition it needs; partial states hold 512 dims."""
+    p = plan(qo=(0, 100, 400), kv=(0, 100, 700), heads=dict(num_qo_heads=hq, **MLA),
+             flags=bia.BIA_PLAN_MLA, split=256)
+    hb = min(hq, 64)
+    T = 64 // hb
+    its = items_of(p)
+    assert max(it["n_tok"] for it in its) == T
+    assert {it["kv_head"] for it in its} == set(range(hq // hb))
+    rows = {}
+    for it in its:
+        for t in range(it["n_tok"]):
+            for j in range(hb):
+                key = (it["q_row0"] + t, it["kv_head"] * hb + j)
+                rows.setdefault(key, []).append(it["kv_begin"])
+    assert len(rows) == 400 * hq
+    for (row, h), parts in rows.items():
+        # request 0: rows 0..99 at positions 0..99; request 1: rows 100..399
+        # at positions 300..599; a row's tile reaches the last position of
+        # its T-token tile (tiles start at the request's first row)
+        base, first_pos, kv_len = (0, 0, 100) if row < 100 else (100, 300, 600)
+        off = row - base
+        tile_last = min(first_pos + off // T * T + T - 1, kv_len - 1)
+        assert sorted(parts) == [256 * k for k in range(tile_last // 256 + 1)]
+    assert p.workspace_bytes >= p.num_states * (512 + 1) * 4
+
+
+def test_mla_plan_rejected_by_the_other_calls():
+    lib = bia.load_library()
+    p = plan(heads=dict(num_qo_heads=16, **MLA), flags=bia.BIA_PLAN_MLA)
+    g = plan()
+    dummy = ctypes.c_void_p(256)
+    st = lib.bia_prefill_paged(ctypes.c_void_p(p.handle), dummy, dummy, dummy, dummy, 1.0,
+                               dummy, None, dummy, p.workspace_bytes, None)
+    assert st == 1 and "MLA" in bia.bia_last_error()
+    st = lib.bia_mla_prefill_paged(ctypes.c_void_p(g.handle), dummy, dummy, dummy, 1.0,
+                                   dummy, None, dummy, g.workspace_bytes, None)
+    assert st == 1 and "BIA_PLAN_MLA" in bia.bia_last_error()
+    st = lib.bia_mla_decode_paged(ctypes.c_void_p(p.handle), dummy, dummy, dummy, 1.0,
+                                  dummy, None, dummy, p.workspace_bytes, None)
+    assert st == 1 and "mode" in bia.bia_last_error()
+    st = lib.bia_append_paged_kv(ctypes.c_void_p(p.handle), dummy, dummy, dummy, dummy,
+                                 dummy, dummy, p.workspace_bytes, None)
+    assert st == 5
+    p.close()
+    g.close()
 
 
 # ------------------------------------------------------------ work lists ---
