@@ -236,6 +236,75 @@ def decode_graph_replay(torch, bia, db, d_pt, stream, dev, ref_out, ref_lse, rep
             "bit_equal_to_planned": same}
 
 
+def mla_flops(qo_lens, kv_lens, num_qo_heads) -> float:
+    """2 * (576 + 512) * Hq per (query row, visible key): scores over the
+    576-dim latent + rope row, values over its first 512 dims."""
+    total = 0
+    for qo, kv in zip(qo_lens, kv_lens):
+        qo, kv = int(qo), int(kv)
+        total += qo * ((kv - qo + 1) + kv) // 2
+    return 2.0 * (576 + 512) * num_qo_heads * total
+
+
+def mla_bytes(kv_lens, num_qo_heads, page_size=16) -> float:
+    """Cached latent rows read once, q in, out and lse out, page ids."""
+    kv = np.asarray(kv_lens, dtype=np.int64)
+    b = kv.sum() * 576 * 2
+    b += len(kv) * num_qo_heads * (576 * 2 + 512 * 2 + 4)
+    b += 4 * ((kv + page_size - 1) // page_size).sum()
+    return float(b)
+
+
+def mla_extra(torch, bia, W, stream, dev, reps=10):
+    """Latent (MLA) attention: causal prefill of 4 x 4096 tokens and decode of
+    64 requests with contexts U[1, 32768], at 16 and 128 q heads (one GPU's
+    heads of a 128-head model under 8-way head parallelism, and all of them).
+    Prefill against the bf16 MFMA peak; decode against HBM bandwidth (bytes
+    of the cached rows read once) and, for 128 heads, also as TFLOP/s."""
+    res = {}
+    for hq in (16, 128):
+        row = {}
+        for mode in ("prefill", "decode"):
+            if mode == "prefill":
+                b = W.mla_prefill(hq, device=dev)
+                m, split = bia.BIA_MODE_PREFILL, bia.BIA_PREFILL_SPLIT
+                fn = bia.bia_mla_prefill_paged
+            else:
+                b = W.mla_decode_batch(64, hq, device=dev)
+                m, split = bia.BIA_MODE_DECODE, bia.BIA_DECODE_SPLIT
+                fn = bia.bia_mla_decode_paged
+            pt = torch.as_tensor(b.page_table, dtype=torch.int32, device=dev)
+            kv = b.k_pool.view(b.num_pages, 16, 576)
+            out = torch.empty(b.q.shape[0], hq, 512, dtype=torch.bfloat16, device=dev)
+            lse = torch.empty(b.q.shape[0], hq, dtype=torch.float32, device=dev)
+            plan = bia.bia_plan_create(m, b.qo_indptr, b.kv_indptr, b.page_table,
+                                       num_qo_heads=hq, num_kv_heads=1, head_dim=576,
+                                       num_pages=b.num_pages, split_size=split,
+                                       flags=bia.BIA_PLAN_MLA)
+            ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            t = Timer(torch, stream)
+            for i in range(reps + 2):
+                s = t.start()
+                fn(plan, b.q, kv, pt, b.sm_scale, out, lse, ws, stream)
+                t.stop(s)
+            torch.cuda.synchronize()
+            t.pairs = t.pairs[2:]
+            ms = t.mean_ms()
+            fl = mla_flops(b.qo_lens(), b.kv_lens(), hq)
+            tf = fl / (ms * 1e-3) / 1e12
+            e = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                 "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            if mode == "decode":
+                gbs = mla_bytes(b.kv_lens(), hq) / (ms * 1e-3) / 1e9
+                e["GB/s"] = round(gbs, 1)
+                e["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+            row[mode] = e
+            plan.close()
+            del b, kv, out, lse, ws, pt
+        res[f"hq{hq}"] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +314,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode batch sweep, the graph-replay decode and the "
                          "copy-bandwidth reference")
+    ap.add_argument("--mla-only", action="store_true",
+                    help="time only the latent (MLA) calls and print their numbers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy a 1 GiB buffer 3 times, so a counter run also "
                          "records a plain copy of known size (HBM-byte calibration)")
@@ -271,6 +342,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.mla_only:
+        print(json.dumps({"mla": mla_extra(torch, bia, W, stream, dev)}), flush=True)
+        return
 
     pb = W.qwen_prefill(device=dev)                       # 8 x 4096, 64K-page pool
     db = W.decode_batch(64, seed=4, num_pages=131072, device=dev)
@@ -339,6 +414,7 @@ def main():
         extras["copy_gbs"] = copy_bandwidth(torch, stream, dev)
         extras["sweep"] = decode_sweep(torch, bia, W, db, d_pt, stream, dev)
         extras["graph"] = decode_graph_replay(torch, bia, db, d_pt, stream, dev, d_out, d_lse)
+        extras["mla"] = mla_extra(torch, bia, W, stream, dev)
 
     p_flops = prefill_flops(pb.qo_lens(), pb.kv_lens(), 32, 128)
     d_bytes = decode_bytes(db.kv_lens(), 32, 8, 128)
@@ -397,6 +473,7 @@ def main():
         result["decode"]["frac_of_copy"] = round(d_gbs / copy, 4)
         result["decode"]["sweep"] = extras["sweep"]
         result["decode"]["graph_replay"] = extras["graph"]
+        result["mla"] = extras["mla"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(pb)
         result["decode"]["cpu_baseline"] = cpu_baseline_decode(db)

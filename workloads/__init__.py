@@ -331,6 +331,25 @@ def decode_batch(batch: int, *, seed: int = 4, num_pages: int = 131072,
                       device=device, **head)
 
 
+def mla_prefill(num_qo_heads: int, device="cpu", batch=4, length=4096, num_pages=16384,
+                seed=12):
+    """Latent-cache prefill: ``batch`` requests of ``length`` tokens, one
+    576-dim cached head shared by ``num_qo_heads`` q heads."""
+    reqs = [Request(length, length, seed * 1000 + r) for r in range(batch)]
+    return make_mla_batch(reqs, num_qo_heads=num_qo_heads, num_pages=num_pages,
+                          batch_seed=seed, device=device)
+
+
+def mla_decode_batch(batch: int, num_qo_heads: int, *, seed: int = 4, num_pages: int = 131072,
+                     device="cpu", max_ctx: int = 32768) -> PagedBatch:
+    """``batch`` latent-cache decode requests with the context lengths of
+    ``decode_batch`` (uniform in [1, max_ctx])."""
+    ctx = decode_context_lengths(batch, seed, max_ctx)
+    reqs = [Request(1, int(c), seed * 100003 + r) for r, c in enumerate(ctx)]
+    return make_mla_batch(reqs, num_qo_heads=num_qo_heads, num_pages=num_pages,
+                          batch_seed=seed + 7919 * batch, device=device)
+
+
 def mixed_decode_lengths(n: int = 128, seed: int = 5, median: int = 4096,
                          sigma: float = 1.0, cap: int = 131072) -> np.ndarray:
     """Lognormal context lengths: round(exp(N(ln median, sigma^2))) in [1, cap]."""
