@@ -194,6 +194,43 @@ __device__ __forceinline__ void lds_dma16_sbase(uint32_t lane_off, const void* b
                : "memory");
 }
 
+// N DMA instructions sharing one M0: instruction r reads global
+// (base - 1024 r) + off[r] + 1024 r = base + off[r] and writes LDS
+// m0 + 1024 r + 16 lane (the immediate offset moves both addresses).
+template <int N>
+__device__ __forceinline__ void dma_page(const uint32_t (&off)[N], uint64_t base, uint32_t m0) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(m0);
+  uint64_t sb[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    const uint64_t b = base - 1024ull * r;
+    sb[r] = join_u64(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                         static_cast<uint32_t>(b >> 32))),
+                     static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b))));
+  }
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %8\n\t"
+        "global_load_lds_dwordx4 %0, %4\n\t"
+        "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %6 offset:2048\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:3072"
+        :
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(sb[0]), "s"(sb[1]),
+          "s"(sb[2]), "s"(sb[3]), "s"(m)
+        : "memory");
+  } else {
+    static_assert(N == 2, "2 or 4 instructions per page");
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "global_load_lds_dwordx4 %0, %2\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:1024"
+        :
+        : "v"(off[0]), "v"(off[1]), "s"(sb[0]), "s"(sb[1]), "s"(m)
+        : "memory");
+  }
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // max over lanes l and l ^ 32
@@ -235,6 +272,7 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TB];  // K0 K1 V0 V1
 
   const WorkItem it = items[blockIdx.x];
+  if (it.n_tok == 0) return;  // padding of the XCD-interleaved launch order
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -285,22 +323,48 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   auto page_id = [&](int32_t pgv, int r) -> int32_t {
     return __builtin_amdgcn_readlane(pgv, (RPI * (4 * r + wave)) >> 4);
   };
-  // A lane's rows within a page and its chunk are the same for every DMA
-  // instruction of every tile (row0 is a multiple of 16 apart between
-  // instructions), so its byte offset from the page base is one constant.
-  const int dma_row = RPI * wave + lane / SLOTS;  // row of instruction 0 (mod 16)
-  const uint32_t dma_lane_off = static_cast<uint32_t>(
-      ((dma_row & 15) * slot_stride + head_off + ((lane % SLOTS) ^ lds_swz<D>(dma_row)) * 8) * 2);
-  auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, int32_t pgv) {
+  // The page ids one wave's DMAs of a tile use, in SGPRs. They are taken out
+  // of the vectors before any DMA of the step is issued and pinned there: the
+  // DMAs are inline asm that the compiler does not count as loads, so a
+  // page-id read placed after them gets a wait on the load counter that would
+  // also wait for the DMAs just issued (a memory round trip every tile).
+  struct TilePages {
+    int32_t id[IPW];  // ragged tiles: page of DMA instruction r
+    int32_t own;      // full tiles: page `wave` of the tile
+  };
+  auto take_pages = [&](int32_t pgv) -> TilePages {
+    TilePages tp;
+#pragma unroll
+    for (int r = 0; r < IPW; ++r) {
+      tp.id[r] = page_id(pgv, r);
+      asm volatile("" : "+s"(tp.id[r]));
+    }
+    tp.own = __builtin_amdgcn_readlane(pgv, wave);
+    asm volatile("" : "+s"(tp.own));
+    return tp;
+  };
+  // Full tiles: wave w fills rows 16 w .. 16 w + 15 (page w of the tile);
+  // instruction r covers rows 16 w + RPI r + lane / SLOTS. All IPW
+  // instructions share one M0 (the wave's 1 KB x IPW of the buffer) and
+  // differ in the immediate offset 1024 r, which moves the LDS destination
+  // and the global address alike, so the global base of instruction r is
+  // taken back by the same amount. A lane's byte offset from the page base
+  // is fixed per instruction for the whole kernel (the swizzle makes it
+  // depend on r). One M0 write per tile and tensor instead of one per DMA.
+  uint32_t dma_off[IPW];
+#pragma unroll
+  for (int r = 0; r < IPW; ++r) {
+    const int row = RPI * r + lane / SLOTS;  // row within the page
+    dma_off[r] = static_cast<uint32_t>(
+        (row * slot_stride + head_off + ((lane % SLOTS) ^ lds_swz<D>(16 * wave + row)) * 8) * 2);
+  }
+  auto issue = [&](const uint16_t* __restrict__ pool, int t, int buf, const TilePages& tp) {
     const int t0 = it.kv_begin + 64 * t;
     if (t0 + 64 <= kv_end) {  // uniform: every row of the tile is a key of the item
-#pragma unroll
-      for (int r = 0; r < IPW; ++r) {
-        const int row0 = RPI * (4 * r + wave);
-        const uint16_t* page_base =
-            pool + static_cast<int64_t>(page_id(pgv, r)) * 16 * slot_stride;
-        lds_dma16_sbase(dma_lane_off, page_base, lds_base + buf * TB + row0 * RB);
-      }
+      const uint64_t page_base = reinterpret_cast<uint64_t>(
+          pool + static_cast<int64_t>(tp.own) * 16 * slot_stride);
+      const uint32_t m0 = lds_base + buf * TB + wave * 16 * RB;
+      dma_page<IPW>(dma_off, page_base, m0);
     } else {
 #pragma unroll
       for (int r = 0; r < IPW; ++r) {
@@ -310,8 +374,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
         const int key = t0 + row;
         const int dst = buf * TB + row0 * RB;
         if (key < kv_end) {
-          const uint16_t* src = pool + (static_cast<int64_t>(page_id(pgv, r)) * 16 +
-                                        (key & 15)) * slot_stride + head_off + chunk * 8;
+          const uint16_t* src = pool + (static_cast<int64_t>(tp.id[r]) * 16 + (key & 15)) *
+                                           slot_stride + head_off + chunk * 8;
           lds_dma16(src, lds_base + dst);
         } else {  // past the item's keys: zero, never stale LDS contents
           *reinterpret_cast<uint4*>(&lds[dst + lane * 16]) = make_uint4(0, 0, 0, 0);
@@ -360,11 +424,16 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   // ---- prologue: K(0), V(0), K(1) by DMA; scores of tile 0 ----
   f32x16 sacc[2];
   int32_t pg_v = pages(0);
-  issue(kp, 0, 0, pg_v);
-  issue(vp, 0, 2, pg_v);
-  pg_v = pages(1);
-  if (n_tiles > 1) issue(kp, 1, 1, pg_v);
-  int32_t pg_k = pages(2);
+  int32_t pg_k = pages(1);
+  {
+    const TilePages p0 = take_pages(pg_v);
+    const TilePages p1 = take_pages(pg_k);
+    issue(kp, 0, 0, p0);
+    issue(vp, 0, 2, p0);
+    if (n_tiles > 1) issue(kp, 1, 1, p1);
+  }
+  pg_v = pg_k;
+  pg_k = pages(2);
   wait_dma();
   __syncthreads();
   scores(sacc, 0);
@@ -403,8 +472,10 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     wait_dma();
     __syncthreads();  // K(j+1), V(j) are in LDS; every wave is done with tile j-1
     if constexpr (kHasNext) {
-      if (j + 2 < n_tiles) issue(kp, j + 2, P, pg_k);
-      issue(vp, j + 1, 3 - P, pg_v);
+      const TilePages kpg = take_pages(pg_k);
+      const TilePages vpg = take_pages(pg_v);
+      if (j + 2 < n_tiles) issue(kp, j + 2, P, kpg);
+      issue(vp, j + 1, 3 - P, vpg);
       pg_v = pg_k;
       pg_k = pages(j + 3);
     }
@@ -929,6 +1000,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
            float* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMlaTileBytes];
   const WorkItem it = items[blockIdx.x];
+  if (it.n_tok == 0) return;  // padding of the XCD-interleaved launch order
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

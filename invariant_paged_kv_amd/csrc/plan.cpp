@@ -1,11 +1,13 @@
 // Host split planner: validates a batch and lays out its work list.
 //
 // The layout is a function of each request's (qo_len, kv_len) alone: q tiles
-// start at the request's first query token and hold 128 / group tokens;
+// start at the request's first query token and hold 128 / group tokens (64 /
+// group for latent plans);
 // split-KV partitions are [k * split, (k + 1) * split) anchored at key 0 of
 // the request (a fixed split size, sglang PR #10417, Modifications; the
 // 128-row q-tile grid, sglang PR #43612, Summary). The launch order of the
-// items (longest first) changes nothing in any result.
+// items (XCD-aware for prefill, longest first for decode) changes nothing in
+// any result.
 //
 // Plain C++: no HIP call, so it runs and is tested without a GPU.
 #include <algorithm>
@@ -52,11 +54,86 @@ static int64_t item_tiles(const WorkItem& w, int32_t split) {
   return ceil_div(end - w.kv_begin, kKvTile);
 }
 
+// Prefill launch order. Workgroup i runs on XCD i mod 8, and each XCD has its
+// own L2; the q tiles of one (request, kv head) pair all read the same K/V
+// pages. So the items are grouped into units (a pair, or for batches with few
+// pairs a round-robin share of a pair's items), units are spread over the 8
+// XCDs by work (largest first, each to the least-loaded XCD), each XCD runs
+// its units one after the other with every unit's items longest first, and
+// the per-XCD lists are interleaved so that launch index 8 s + x is item s of
+// XCD x (shorter lists padded with empty items). The XCD's running
+// workgroups then share one pair's pages in its L2 instead of thrashing it
+// with all pairs at once. The order changes no result.
+constexpr int kXcds = 8;
+constexpr size_t kMinUnits = 4 * kXcds;
+
+static void order_for_xcds(PlanData& d, const std::vector<int64_t>& unit_of) {
+  const int32_t split = d.split;
+  const size_t n = d.items.size();
+  if (n == 0) return;
+  // units in order of first appearance
+  std::vector<std::vector<size_t>> units;
+  {
+    std::vector<std::pair<int64_t, size_t>> key(n);
+    for (size_t i = 0; i < n; ++i) key[i] = {unit_of[i], i};
+    std::stable_sort(key.begin(), key.end(),
+                     [](const auto& a, const auto& b) { return a.first < b.first; });
+    for (size_t i = 0; i < n; ++i) {
+      if (i == 0 || key[i].first != key[i - 1].first) units.emplace_back();
+      units.back().push_back(key[i].second);
+    }
+  }
+  auto longest_first = [&](std::vector<size_t>& v) {
+    std::stable_sort(v.begin(), v.end(), [&](size_t a, size_t b) {
+      return item_tiles(d.items[a], split) > item_tiles(d.items[b], split);
+    });
+  };
+  for (auto& u : units) longest_first(u);
+  if (units.size() < kMinUnits) {  // few pairs: deal each pair's items into k shares
+    const size_t k = (kMinUnits + units.size() - 1) / units.size();
+    std::vector<std::vector<size_t>> shares;
+    for (const auto& u : units) {
+      const size_t first = shares.size();
+      shares.resize(first + std::min(k, u.size()));
+      for (size_t i = 0; i < u.size(); ++i) shares[first + i % k].push_back(u[i]);
+    }
+    units.swap(shares);
+  }
+  std::vector<int64_t> work(units.size(), 0);
+  for (size_t u = 0; u < units.size(); ++u)
+    for (size_t i : units[u]) work[u] += item_tiles(d.items[i], split);
+  std::vector<size_t> by_work(units.size());
+  for (size_t u = 0; u < units.size(); ++u) by_work[u] = u;
+  std::stable_sort(by_work.begin(), by_work.end(),
+                   [&](size_t a, size_t b) { return work[a] > work[b]; });
+  std::vector<std::vector<size_t>> xcd(kXcds);
+  int64_t load[kXcds] = {0};
+  for (size_t u : by_work) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    load[best] += work[u];
+    xcd[best].insert(xcd[best].end(), units[u].begin(), units[u].end());
+  }
+  size_t longest = 0;
+  for (const auto& l : xcd) longest = std::max(longest, l.size());
+  std::vector<WorkItem> out;
+  out.reserve(longest * kXcds);
+  const WorkItem empty{0, 0, 0, 0, 0, 0, 0, -1};
+  for (size_t s = 0; s < longest; ++s)
+    for (int x = 0; x < kXcds; ++x)
+      out.push_back(s < xcd[x].size() ? d.items[xcd[x][s]] : empty);
+  // trailing padding launches nothing useful: drop it
+  while (!out.empty() && out.back().n_tok == 0) out.pop_back();
+  d.items.swap(out);
+}
+
 static bia_status build(PlanData& d, const int32_t* qo_indptr,
                         const int32_t* kv_indptr) {
   const bool decode = d.mode == BIA_MODE_DECODE;
   const int32_t g = d.group;
   const int32_t T = decode ? 1 : d.tile_tokens;
+  std::vector<int64_t> unit_of;  // (request, kv head) of each item
   int64_t page_off = 0;
   for (int32_t r = 0; r < d.batch; ++r) {
     const int32_t qo_len = qo_indptr[r + 1] - qo_indptr[r];
@@ -86,6 +163,7 @@ static bia_status build(PlanData& d, const int32_t* qo_indptr,
                      static_cast<int32_t>(page_off), h, k * d.split,
                      base < 0 ? -1 : static_cast<int32_t>(base + int64_t(k) * rows)};
           d.items.push_back(w);
+          unit_of.push_back(static_cast<int64_t>(r) * d.num_kv_heads + h);
         }
       }
     }
@@ -93,8 +171,14 @@ static bia_status build(PlanData& d, const int32_t* qo_indptr,
   }
   if (d.items.size() > static_cast<size_t>(INT32_MAX))
     return fail(BIA_ERR_SHAPE, "too many work items");
-  // Longest items first, so the tail of the launch is short work; a stable
-  // sort keeps the plan itself deterministic.
+  if (!decode) {
+    order_for_xcds(d, unit_of);
+    if (d.items.size() > static_cast<size_t>(INT32_MAX))
+      return fail(BIA_ERR_SHAPE, "too many work items");
+    return BIA_OK;
+  }
+  // Decode items share no pages: longest first, so the tail of the launch is
+  // short work; a stable sort keeps the plan itself deterministic.
   const int32_t split = d.split;
   std::stable_sort(d.items.begin(), d.items.end(),
                    [split](const WorkItem& a, const WorkItem& b) {

@@ -222,7 +222,50 @@ FIELDS = ["q_row0", "n_tok", "pos0", "kv_len", "page_off", "kv_head", "kv_begin"
 
 
 def items_of(p):
-    return [dict(zip(FIELDS, map(int, row))) for row in p.items()]
+    """The plan's work items in launch order, without the empty items that pad
+    the prefill's per-XCD lists."""
+    return [dict(zip(FIELDS, map(int, row))) for row in p.items() if row[1] > 0]
+
+
+def item_tiles(it, split):
+    last = it["pos0"] + it["n_tok"] - 1
+    end = min(it["kv_begin"] + split, last + 1)
+    return -(-(end - it["kv_begin"]) // 64)
+
+
+@pytest.mark.parametrize("reqs,heads,split", [
+    (dict(qo=(0, 4096, 8192), kv=(0, 4096, 8192)), QWEN, 4096),       # 16 pairs
+    (dict(qo=(0, 1000), kv=(0, 3000)), dict(num_qo_heads=4, num_kv_heads=1, head_dim=64),
+     1024),                                                            # 1 pair, shared out
+    (dict(qo=(0, 5, 905, 1000, 3000), kv=(0, 5, 2000, 2095, 9000)), QWEN, 4096),
+])
+def test_prefill_launch_order_is_xcd_interleaved(reqs, heads, split):
+    """Launch index 8 s + x runs on XCD x. Every item appears once; the
+    per-XCD lists carry near-equal work (within the largest unit); on each
+    XCD the items of one (request, kv head) pair are contiguous unless pairs
+    were shared out; padding is empty items only."""
+    p = plan(heads=heads, split=split, num_pages=4096, **reqs)
+    rows = p.items()
+    ref = plan(heads=heads, split=split, num_pages=4096, **reqs)
+    real = [tuple(map(int, r)) for r in rows if r[1] > 0]
+    assert len(set(real)) == len(real)
+    assert all(tuple(r) == (0, 0, 0, 0, 0, 0, 0, -1) for r in rows if r[1] == 0)
+    assert sorted(real) == sorted(tuple(map(int, r)) for r in ref.items() if r[1] > 0)
+    xcd_work = [0] * 8
+    xcd_pairs = [[] for _ in range(8)]
+    for i, r in enumerate(rows):
+        it = dict(zip(FIELDS, map(int, r)))
+        if it["n_tok"] == 0:
+            continue
+        xcd_work[i % 8] += item_tiles(it, split)
+        pair = (it["kv_len"], it["page_off"], it["kv_head"])
+        if not xcd_pairs[i % 8] or xcd_pairs[i % 8][-1] != pair:
+            xcd_pairs[i % 8].append(pair)
+    n_pairs = len({(it["page_off"], it["kv_head"]) for it in items_of(p)})
+    assert max(xcd_work) - min(xcd_work) <= max(xcd_work) // 2 + 64
+    if n_pairs >= 32:
+        for seq in xcd_pairs:          # each pair visited once per XCD
+            assert len(seq) == len(set(seq))
 
 
 def request_layout(p, q_row0, kv_head=0):
