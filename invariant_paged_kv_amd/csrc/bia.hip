@@ -1034,11 +1034,10 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   // Tile loads: thread t moves pieces i = t + 256 u: key row i / 72, piece
   // i % 72. A tile's 32 keys are two pages; their ids come from one vector
   // load made a tile ahead (lane l holds page l % 2).
-  uint4 stage[kMlaLoads];
   auto page_pair = [&](int t) -> int32_t {
     return pt[min(((it.kv_begin + kMlaKeys * t) >> 4) + (lane & 1), last_page)];
   };
-  auto load_tile = [&](int t, int32_t pgv) {
+  auto load_tile = [&](uint4 (&stage)[kMlaLoads], int t, int32_t pgv) {
     const int t0 = it.kv_begin + kMlaKeys * t;
     const int32_t pa = __builtin_amdgcn_readlane(pgv, 0);
     const int32_t pb = __builtin_amdgcn_readlane(pgv, 1);
@@ -1056,7 +1055,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
       stage[u] = w;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const uint4 (&stage)[kMlaLoads], int buf) {
 #pragma unroll
     for (int u = 0; u < kMlaLoads; ++u) {
       const int i = tid + kThreads * u;
@@ -1071,7 +1070,12 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
 #pragma unroll
   for (int b = 0; b < kMlaDv / 16; ++b) o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // A wave whose rows are all past the item's tokens (decode with fewer than
+  // 64 rows, a request's last tile) skips the MFMAs; it still loads, stores
+  // and meets every barrier.
+  const bool wave_active = ((wave * 16) >> hb_shift) < it.n_tok;
   auto compute = [&](int j, int buf) {
+    if (!wave_active) return;
     const uint8_t* base = &lds[buf * kMlaTileBytes];
     // ---- scores: S^T for keys 16 kb + m (m = n16) x the wave's 16 rows ----
     f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -1135,19 +1139,30 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     }
   };
 
+  // Two register stages: tile t's loads land in stage t % 2. While tile j
+  // computes, the loads of tile j+2 are in flight and tile j+1 (loaded a
+  // step earlier) waits to go to LDS, so each load has a whole step of cover.
+  uint4 st_a[kMlaLoads], st_b[kMlaLoads];
   int32_t pgv = page_pair(0);
-  load_tile(0, pgv);
-  store_tile(0);
+  load_tile(st_a, 0, pgv);
+  store_tile(st_a, 0);
   pgv = page_pair(1);
+  if (n_tiles > 1) load_tile(st_b, 1, pgv);
+  pgv = page_pair(2);
   __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) {
-      load_tile(j + 1, pgv);
-      pgv = page_pair(j + 2);
+  // cur: stage of tile j (already in LDS), reused for tile j+2; nxt: tile j+1.
+  auto step = [&](int j, uint4 (&cur)[kMlaLoads], const uint4 (&nxt)[kMlaLoads]) {
+    if (j + 2 < n_tiles) {
+      load_tile(cur, j + 2, pgv);
+      pgv = page_pair(j + 3);
     }
     compute(j, j & 1);
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);  // the buffer tile j-1 used
+    if (j + 1 < n_tiles) store_tile(nxt, (j + 1) & 1);  // the buffer tile j-1 used
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, st_a, st_b);
+    if (j + 1 < n_tiles) step(j + 1, st_b, st_a);
   }
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----
