@@ -93,6 +93,8 @@ typedef enum bia_mode {
 #define BIA_PLAN_MLA 0x2u
 #define BIA_MLA_QK_DIM 576
 #define BIA_MLA_V_DIM 512
+/* Largest split size of an MLA plan (the item's page list is held on chip). */
+#define BIA_MLA_MAX_SPLIT 16384
 
 typedef struct bia_plan bia_plan; /* opaque, library-owned */
 

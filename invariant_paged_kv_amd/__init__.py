@@ -19,7 +19,8 @@ Typical use::
 from __future__ import annotations
 
 from ._lib import (BIA_DECODE_SPLIT, BIA_KV_TILE, BIA_MODE_DECODE,
-                   BIA_MLA_QK_DIM, BIA_MLA_V_DIM, BIA_MODE_PREFILL, BIA_PAGE_SIZE,
+                   BIA_MLA_MAX_SPLIT, BIA_MLA_QK_DIM, BIA_MLA_V_DIM, BIA_MODE_PREFILL,
+                   BIA_PAGE_SIZE,
                    BIA_PLAN_MLA, BIA_PLAN_STRICT_CHUNK_ALIGN,
                    BIA_PREFILL_SPLIT, BIA_Q_TILE_ROWS, BiaError, DecodeGraph, Plan,
                    bia_append_paged_kv, bia_decode_graph_create,
@@ -33,7 +34,8 @@ from ._lib import (BIA_DECODE_SPLIT, BIA_KV_TILE, BIA_MODE_DECODE,
                    load_library)
 
 __all__ = [
-    "BIA_DECODE_SPLIT", "BIA_KV_TILE", "BIA_MLA_QK_DIM", "BIA_MLA_V_DIM", "BIA_MODE_DECODE",
+    "BIA_DECODE_SPLIT", "BIA_KV_TILE", "BIA_MLA_MAX_SPLIT", "BIA_MLA_QK_DIM", "BIA_MLA_V_DIM",
+    "BIA_MODE_DECODE",
     "BIA_MODE_PREFILL", "BIA_PAGE_SIZE", "BIA_PLAN_MLA", "BIA_PLAN_STRICT_CHUNK_ALIGN", "BIA_PREFILL_SPLIT", "BIA_Q_TILE_ROWS",
     "BiaError", "DecodeGraph", "Plan", "bia_append_paged_kv", "bia_decode_graph_create",
     "bia_decode_graph_destroy", "bia_decode_graph_read_flags", "bia_decode_graph_run",

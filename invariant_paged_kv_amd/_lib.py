@@ -27,6 +27,7 @@ BIA_PLAN_STRICT_CHUNK_ALIGN = 0x1
 BIA_PLAN_MLA = 0x2
 BIA_MLA_QK_DIM = 576
 BIA_MLA_V_DIM = 512
+BIA_MLA_MAX_SPLIT = 16384
 
 _STATUS = {0: "BIA_OK", 1: "BIA_ERR_INVALID_ARG", 2: "BIA_ERR_SHAPE",
            3: "BIA_ERR_PAGE_RANGE", 4: "BIA_ERR_WORKSPACE", 5: "BIA_ERR_UNSUPPORTED",

@@ -944,10 +944,18 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
 //
 // One workgroup = one WorkItem = 64 q rows (64 / hb tokens x hb heads of one
 // head block, hb = min(Hq, 64); the plan's "kv head" is the head block) over
-// one split-KV partition; 4 waves x 16 rows. Per 32-key tile, staged in LDS
-// by all threads (global loads of tile j+1 in flight while tile j computes;
-// rows padded to 1168 bytes, which keeps both the K-operand reads and the
-// transposing V reads on distinct banks):
+// one split-KV partition; 4 waves x 16 rows. Per 32-key tile:
+//   K/V staging: the tile's two pages (16 rows x 1152 bytes each, contiguous
+//   in the pool) are copied to LDS by DMA, 18 instructions of 1 KB per page
+//   spread over the waves. LDS rows are unpadded; the 16-byte chunk c of
+//   tile row r sits at slot c ^ f(r), f(r) = (r / 2) % 8, which permutes
+//   chunks inside aligned groups of 8 and keeps the K-operand reads (16 rows,
+//   one chunk) and the transposing V reads on distinct banks. Four buffers:
+//   the DMAs of tiles j+1 .. j+3 are in flight while tile j computes, and a
+//   wave waits only for its own DMAs of tile j (counted waits). Keys past
+//   the partition's end read a valid key of the same page instead; their
+//   scores are masked, so they add exact zeros. Page ids come from an LDS
+//   copy of the item's page list made once per item.
 //   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys as M, the wave's 16 rows
 //   as N, 576 dims as 18 k-steps; layout checked on the GPU with an exact
 //   integer probe: A[m][k]: m = l % 16, k = 8 (l / 16) + e; B[k][n]:
@@ -968,12 +976,15 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMlaDk = BIA_MLA_QK_DIM;
 constexpr int kMlaDv = BIA_MLA_V_DIM;
-constexpr int kMlaKeys = 32;                              // keys per tile
-constexpr int kMlaRowBytes = kMlaDk * 2 + 16;             // padded LDS row
-constexpr int kMlaTileBytes = kMlaKeys * kMlaRowBytes;    // 37376
-constexpr int kMlaChunks = kMlaDk / 8;                    // 16-byte pieces per row
-constexpr int kMlaLoads = kMlaKeys * kMlaChunks / kThreads;  // per thread per tile
-static_assert(kMlaKeys * kMlaChunks % kThreads == 0, "tile loads split evenly");
+constexpr int kMlaKeys = 32;                            // keys per tile
+constexpr int kMlaRowBytes = kMlaDk * 2;                // 1152, unpadded
+constexpr int kMlaPageBytes = 16 * kMlaRowBytes;        // 18432: one page
+constexpr int kMlaTileBytes = 2 * kMlaPageBytes;        // 36864
+constexpr int kMlaBufs = 4;
+constexpr int kMlaPageDma = kMlaPageBytes / 1024;       // 18 DMA instructions per page
+constexpr int kMlaDmaPerWave = (kMlaPageDma + 3) / 4;   // instructions i = wave + 4 k
+constexpr int kMlaMaxPages = BIA_MLA_MAX_SPLIT / 16;    // page list held in LDS
+static_assert(kMlaPageBytes % 1024 == 0, "a page is whole DMA instructions");
 
 // max and sum over the lanes n, n ^ 16, n ^ 32, n ^ 48 (symmetric: every lane
 // of the four gets the same bits)
@@ -992,13 +1003,29 @@ __device__ __forceinline__ float quad_sum(float x) {
   return a + b;
 }
 
+// Slot of 16-byte chunk c in tile row r.
+__device__ __forceinline__ int mla_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Wait until at most n of this wave's DMAs are outstanding (n a multiple of
+// the per-tile count; vmcnt counts in issue order).
+__device__ __forceinline__ void mla_wait(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+  }
+}
+
 __global__ void __launch_bounds__(kThreads, 1)
 mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
            const uint16_t* __restrict__ kvp, const int32_t* __restrict__ page_table,
            float scale_log2, int num_qo_heads, int hb_shift, int split,
            uint16_t* __restrict__ out, float* __restrict__ lse_out,
            float* __restrict__ o_part, float* __restrict__ lse_part) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMlaTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMlaBufs * kMlaTileBytes];
+  __shared__ int32_t lds_pages[kMlaMaxPages];
   const WorkItem it = items[blockIdx.x];
   if (it.n_tok == 0) return;  // padding of the XCD-interleaved launch order
   const int tid = threadIdx.x;
@@ -1028,39 +1055,57 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   const int last = it.pos0 + it.n_tok - 1;
   const int kv_end = min(it.kv_begin + split, last + 1);
   const int n_tiles = (kv_end - it.kv_begin + kMlaKeys - 1) / kMlaKeys;
-  const int32_t* pt = page_table + it.page_off;
-  const int last_page = (kv_end - 1) >> 4;
+  const int first_page = it.kv_begin >> 4;
+  const int n_pages = ((kv_end - 1) >> 4) - first_page + 1;  // <= kMlaMaxPages (plan check)
+  const int32_t* pt = page_table + it.page_off + first_page;
+  for (int i = tid; i < n_pages; i += kThreads) lds_pages[i] = pt[i];
+  // Q and the page list are waited for here, before any DMA is in flight:
+  // the DMAs are inline asm the compiler does not count, and a later
+  // compiler wait for these loads would also wait for the DMAs.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
+  __syncthreads();
 
-  // Tile loads: thread t moves pieces i = t + 256 u: key row i / 72, piece
-  // i % 72. A tile's 32 keys are two pages; their ids come from one vector
-  // load made a tile ahead (lane l holds page l % 2).
-  auto page_pair = [&](int t) -> int32_t {
-    return pt[min(((it.kv_begin + kMlaKeys * t) >> 4) + (lane & 1), last_page)];
-  };
-  auto load_tile = [&](uint4 (&stage)[kMlaLoads], int t, int32_t pgv) {
+  // DMA of tile t into buffer t % 4: instruction i (0..17) of page half ph
+  // copies LDS bytes ph * 18432 + 1024 i + 16 lane .. + 15 of the tile, which
+  // hold tile row r = 16 ph + (1024 i + 16 lane) / 1152 at slot
+  // ((1024 i + 16 lane) % 1152) / 16 = mla_slot(r, c) for chunk c. Wave w
+  // issues i = w, w + 4, ..: 10 instructions per tile for waves 0-1, 8 for
+  // waves 2-3 (the same count for every tile, ragged ones included).
+  const uint32_t lds_base = lds_offset(lds);
+  uint32_t dma_off[kMlaDmaPerWave];  // byte offset of this lane's chunk in its page
+  int dma_row[kMlaDmaPerWave];       // its row in the page
+#pragma unroll
+  for (int k = 0; k < kMlaDmaPerWave; ++k) {
+    const int i = wave + 4 * k;
+    const int p = 1024 * i + 16 * lane;
+    const int rr = p / kMlaRowBytes;
+    const int c = mla_slot(rr, (p % kMlaRowBytes) / 16);  // the slot map is an involution
+    dma_row[k] = rr;
+    dma_off[k] = static_cast<uint32_t>(rr * kMlaRowBytes + c * 16);
+  }
+  const int dma_count = 2 * ((kMlaPageDma - wave + 3) / 4);  // 10 or 8 per tile
+  auto issue = [&](int t) {
     const int t0 = it.kv_begin + kMlaKeys * t;
-    const int32_t pa = __builtin_amdgcn_readlane(pgv, 0);
-    const int32_t pb = __builtin_amdgcn_readlane(pgv, 1);
+    const bool ragged = t0 + kMlaKeys > kv_end;
+    const int last_slot = (kv_end - 1) & 15;
 #pragma unroll
-    for (int u = 0; u < kMlaLoads; ++u) {
-      const int i = tid + kThreads * u;
-      const int row = i / kMlaChunks;
-      const int piece = i % kMlaChunks;
-      const int key = t0 + row;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (key < kv_end) {  // past the item's keys: zero, never stale LDS contents
-        const int64_t page = row < 16 ? pa : pb;
-        w = *reinterpret_cast<const uint4*>(kvp + (page * 16 + (key & 15)) * kMlaDk + piece * 8);
+    for (int ph = 0; ph < 2; ++ph) {
+      const int pi = min(2 * t + ph, n_pages - 1);
+      const int32_t page = __builtin_amdgcn_readfirstlane(lds_pages[pi]);
+      const uint16_t* pbase = kvp + static_cast<int64_t>(page) * 16 * kMlaDk;
+      const uint32_t buf_lds = lds_base + (t % kMlaBufs) * kMlaTileBytes + ph * kMlaPageBytes;
+#pragma unroll
+      for (int k = 0; k < kMlaDmaPerWave; ++k) {
+        const int i = wave + 4 * k;
+        if (i < kMlaPageDma) {  // wave-uniform
+          uint32_t off = dma_off[k];
+          if (ragged && t0 + 16 * ph + dma_row[k] >= kv_end)  // past the keys: a valid key's chunk
+            off = static_cast<uint32_t>(last_slot * kMlaRowBytes) + off % kMlaRowBytes;
+          lds_dma16_sbase(off, pbase, buf_lds + 1024 * i);
+        }
       }
-      stage[u] = w;
-    }
-  };
-  auto store_tile = [&](const uint4 (&stage)[kMlaLoads], int buf) {
-#pragma unroll
-    for (int u = 0; u < kMlaLoads; ++u) {
-      const int i = tid + kThreads * u;
-      *reinterpret_cast<uint4*>(&lds[buf * kMlaTileBytes + (i / kMlaChunks) * kMlaRowBytes +
-                                     (i % kMlaChunks) * 16]) = stage[u];
     }
   };
 
@@ -1070,25 +1115,59 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
 #pragma unroll
   for (int b = 0; b < kMlaDv / 16; ++b) o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // K operand of k-step s, key block kb: tile row 16 kb + n16 (f depends on
+  // n16 only), chunk 4 s + g4 -> slot 8 (s / 2) + ((4 (s % 2) + g4) ^ f).
+  const int fk = (n16 >> 1) & 7;
+  const int k_off[2] = {n16 * kMlaRowBytes + 16 * ((0 + g4) ^ fk),
+                        n16 * kMlaRowBytes + 16 * ((4 + g4) ^ fk)};
+  // V^T operand of dim block b: rows 4 g4 + n16 / 4 (+ 16), dims 16 b + 4 (n16 % 4):
+  // chunk 2 b + h (h = (n16 % 4) / 2), byte (n16 % 2) * 8 in it -> slot
+  // 8 (b / 4) + ((2 (b % 4) + h) ^ f).
+  const int vr = 4 * g4 + (n16 >> 2);
+  const int fv = (vr >> 1) & 7;
+  const int vh = (n16 & 3) >> 1;
+  int v_off[4];
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4)
+    v_off[b4] = vr * kMlaRowBytes + 16 * ((2 * b4 + vh) ^ fv) + 8 * (n16 & 1);
+
   // A wave whose rows are all past the item's tokens (decode with fewer than
-  // 64 rows, a request's last tile) skips the MFMAs; it still loads, stores
+  // 64 rows, a request's last tile) skips the MFMAs; it still issues its DMAs
   // and meets every barrier.
   const bool wave_active = ((wave * 16) >> hb_shift) < it.n_tok;
   auto compute = [&](int j, int buf) {
     if (!wave_active) return;
     const uint8_t* base = &lds[buf * kMlaTileBytes];
     // ---- scores: S^T for keys 16 kb + m (m = n16) x the wave's 16 rows ----
+    // MFMA i = 2 s + kb; its K fragment is read kAhead MFMAs earlier (ring of
+    // kRing registers), each slot fenced so the reads stay ahead.
+    constexpr int kAhead = 6, kRing = 8, kNs = 2 * (kMlaDk / 32);
+    auto kfrag = [&](int i) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                            base + (i & 1) * kMlaPageBytes +
+                                            k_off[(i >> 1) & 1] + 128 * (i >> 2)));
+    };
     f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-    const uint8_t* kb0 = base + n16 * kMlaRowBytes + g4 * 16;
+    bf16x8 kf[kRing];
 #pragma unroll
-    for (int s = 0; s < kMlaDk / 32; ++s) {
+    for (int i = 0; i < kAhead; ++i) kf[i] = kfrag(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kb0 + kb * 16 * kMlaRowBytes + s * 64);
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[s],
-                                                         sc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < kNs; ++i) {
+      sc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[i % kRing], qf[i >> 1], sc[i & 1],
+                                                          0, 0, 0);
+      if (i + kAhead < kNs) kf[(i + kAhead) % kRing] = kfrag(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments go out before the softmax (they do not need P)
+    auto vfrag = [&](int b) -> bf16x8 {
+      const uint8_t* vb = base + v_off[b & 3] + 128 * (b >> 2);
+      const uint2 lo = lds_read_tr16(vb);
+      const uint2 hi = lds_read_tr16(vb + kMlaPageBytes);
+      return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    bf16x8 vf[kRing];
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) vf[b] = vfrag(b);
     const int t0 = it.kv_begin + kMlaKeys * j;
     if (t0 + kMlaKeys - 1 > wave_pos0) {  // wave-uniform: some key is past some row
 #pragma unroll
@@ -1126,43 +1205,24 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     }
     lsum += psum;
     m = m_new;
-    // ---- O^T += V^T P^T: 32 blocks of 16 value dims ----
-    const uint8_t* v0 = base + (4 * g4 + (n16 >> 2)) * kMlaRowBytes + (n16 & 3) * 8;
-    const uint8_t* v1 = v0 + 16 * kMlaRowBytes;
+    // ---- O^T += V^T P^T: 32 blocks of 16 value dims, reads kAhead ahead ----
 #pragma unroll
     for (int b = 0; b < kMlaDv / 16; ++b) {
-      const uint2 lo = lds_read_tr16(v0 + b * 32);
-      const uint2 hi = lds_read_tr16(v1 + b * 32);
-      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)),
-          __builtin_bit_cast(bf16x8, pw), o[b], 0, 0, 0);
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[b % kRing], __builtin_bit_cast(bf16x8, pw),
+                                                     o[b], 0, 0, 0);
+      if (b + kAhead < kMlaDv / 16) vf[(b + kAhead) % kRing] = vfrag(b + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Two register stages: tile t's loads land in stage t % 2. While tile j
-  // computes, the loads of tile j+2 are in flight and tile j+1 (loaded a
-  // step earlier) waits to go to LDS, so each load has a whole step of cover.
-  uint4 st_a[kMlaLoads], st_b[kMlaLoads];
-  int32_t pgv = page_pair(0);
-  load_tile(st_a, 0, pgv);
-  store_tile(st_a, 0);
-  pgv = page_pair(1);
-  if (n_tiles > 1) load_tile(st_b, 1, pgv);
-  pgv = page_pair(2);
-  __syncthreads();
-  // cur: stage of tile j (already in LDS), reused for tile j+2; nxt: tile j+1.
-  auto step = [&](int j, uint4 (&cur)[kMlaLoads], const uint4 (&nxt)[kMlaLoads]) {
-    if (j + 2 < n_tiles) {
-      load_tile(cur, j + 2, pgv);
-      pgv = page_pair(j + 3);
-    }
-    compute(j, j & 1);
-    if (j + 1 < n_tiles) store_tile(nxt, (j + 1) & 1);  // the buffer tile j-1 used
-    __syncthreads();
-  };
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(j, st_a, st_b);
-    if (j + 1 < n_tiles) step(j + 1, st_b, st_a);
+  // DMAs of tiles 0 .. 2 ahead of the loop; tile j+3 goes into the buffer of
+  // tile j-1 once every wave has passed the barrier that follows tile j-1.
+  for (int t = 0; t < min(n_tiles, kMlaBufs - 1); ++t) issue(t);
+  for (int j = 0; j < n_tiles; ++j) {
+    mla_wait(dma_count * min(kMlaBufs - 2, n_tiles - 1 - j));  // this wave's tile-j DMAs done
+    __syncthreads();  // every wave's are; every wave is done with tile j-1
+    if (j + kMlaBufs - 1 < n_tiles) issue(j + kMlaBufs - 1);
+    compute(j, j % kMlaBufs);
   }
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----

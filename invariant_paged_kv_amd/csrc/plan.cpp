@@ -252,6 +252,9 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
       return fail(BIA_ERR_INVALID_ARG,
                   "split_size %d must be a positive multiple of the %d-key KV tile",
                   split_size, kKvTile);
+    if (split_size > BIA_MLA_MAX_SPLIT)
+      return fail(BIA_ERR_UNSUPPORTED, "MLA split_size %d above %d", split_size,
+                  BIA_MLA_MAX_SPLIT);
     group = std::min(num_qo_heads, kMlaTileRows);  // q heads per head block
   } else {
     const bia_status shape_st =

@@ -159,6 +159,16 @@ def test_mla_plan_validation(heads, status):
     assert str(e.value).startswith(status), str(e.value)
 
 
+def test_mla_split_limit():
+    """The item's page list is held on chip: MLA splits above
+    BIA_MLA_MAX_SPLIT are rejected."""
+    heads = dict(num_qo_heads=16, **MLA)
+    plan(heads=heads, flags=bia.BIA_PLAN_MLA, split=bia.BIA_MLA_MAX_SPLIT).close()
+    with pytest.raises(bia.BiaError) as e:
+        plan(heads=heads, flags=bia.BIA_PLAN_MLA, split=bia.BIA_MLA_MAX_SPLIT + 64)
+    assert str(e.value).startswith("BIA_ERR_UNSUPPORTED")
+
+
 def test_mla_plan_without_flag_rejects_576():
     with pytest.raises(bia.BiaError) as e:
         plan(heads=dict(num_qo_heads=16, **MLA))
