@@ -87,6 +87,27 @@ def test_mla_decode_parity(hq):
     mla_parity(b, out, lse, f"mla decode hq={hq}")
 
 
+def test_mla_many_partitions_hq32():
+    """32 q heads (two tokens per 64-row tile) at split 64: rows span up to
+    ten partitions, merged in fixed order at 512 dims; ragged lengths."""
+    reqs = [W.Request(67, 600, 981), W.Request(3, 64, 982), W.Request(1, 65, 983),
+            W.Request(130, 130, 984)]
+    say("mla hq=32 split=64")
+    b = W.make_mla_batch(reqs, num_qo_heads=32, num_pages=128, batch_seed=71, device=DEV)
+    out, lse = run_mla(b, split=64)
+    mla_parity(b, out, lse, "mla prefill hq=32 split=64")
+
+
+def test_mla_decode_hq8():
+    """8 q heads: half of one wave's rows are heads, the rest and three waves
+    are idle rows."""
+    reqs = [W.Request(1, c, 990 + i) for i, c in enumerate([1, 31, 32, 33, 2047, 4100])]
+    say("mla decode hq=8")
+    b = W.make_mla_batch(reqs, num_qo_heads=8, num_pages=512, batch_seed=73, device=DEV)
+    out, lse = run_mla(b, mode=bia.BIA_MODE_DECODE)
+    mla_parity(b, out, lse, "mla decode hq=8")
+
+
 @pytest.mark.parametrize("hq", [8, 64])
 def test_mla_one_key_is_the_value(hq):
     """A row that sees one key returns that key's first 512 dims exactly (its
