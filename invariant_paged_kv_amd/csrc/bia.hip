@@ -1255,6 +1255,207 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// Latent (MLA) decode with at most 16 q heads: one wave per work item (the
+// item's q heads are rows 0 .. Hq - 1 of the wave's 16), four consecutive
+// items per workgroup (measured faster than spreading the items over at
+// least one workgroup per CU), no workgroup barrier. Each wave streams its partition in
+// 16-key tiles (one page each) through two LDS buffers of its own (DMA,
+// counted waits, the same swizzled unpadded rows as mla_kernel):
+//   S^T = K Q^T: 18 v_mfma_f32_16x16x32_bf16 (keys as M, rows as N);
+//   online softmax per row over the four lanes that hold it;
+//   O^T += V^T P^T: 32 v_mfma_f32_16x16x16_bf16, one per 16 value dims. The
+//   16x16x16 B operand (k = 4 (l / 16) + e) is exactly the score MFMA's
+//   output layout, so P goes in as the scores left it, and V^T is one
+//   transposing read per MFMA.
+// Rows past the partition's end read a valid key of the same page; their
+// scores are masked. Per-row arithmetic depends only on the item, so decode
+// stays batch-invariant (it differs from prefill's 32-key tiles).
+// ---------------------------------------------------------------------------
+constexpr int kMlaDecTileKeys = 16;
+constexpr int kMlaDecMaxPages = 128;  // page list per wave: splits up to 2048 keys
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void mla_dec_wait(bool next_in_flight) {
+  if (next_in_flight) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ void __launch_bounds__(kThreads, 1)
+mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
+                  const uint16_t* __restrict__ q, const uint16_t* __restrict__ kvp,
+                  const int32_t* __restrict__ page_table, float scale_log2, int num_qo_heads,
+                  int hb, int split, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                  float* __restrict__ o_part, float* __restrict__ lse_part) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4][2][kMlaPageBytes];
+  __shared__ int32_t lds_pages[4][kMlaDecMaxPages];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= n_items) return;  // no barrier below: waves are independent
+  const WorkItem it = items[item];
+  if (it.n_tok == 0) return;
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;  // row: q head kv_head * hb + n16 when n16 < hb
+  const bool row_valid = n16 < hb;
+  const int pos = row_valid ? it.pos0 : -1;
+  const int64_t row_idx =
+      static_cast<int64_t>(it.q_row0) * num_qo_heads + it.kv_head * hb + n16;
+
+  bf16x8 qf[kMlaDk / 32];
+#pragma unroll
+  for (int s = 0; s < kMlaDk / 32; ++s) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row_valid)
+      w = *reinterpret_cast<const uint4*>(q + row_idx * kMlaDk + 32 * s + 8 * g4);
+    qf[s] = __builtin_bit_cast(bf16x8, w);
+  }
+  const int kv_end = min(it.kv_begin + split, it.pos0 + 1);
+  const int n_tiles = (kv_end - it.kv_begin + kMlaDecTileKeys - 1) / kMlaDecTileKeys;
+  const int32_t* pt = page_table + it.page_off + (it.kv_begin >> 4);
+  int32_t* my_pages = lds_pages[wave];
+  for (int i = lane; i < n_tiles; i += 64) my_pages[i] = pt[i];  // one page per tile
+  // Q and the page ids are waited for before any DMA is in flight.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
+
+  // DMA of tile t: 18 instructions of 1 KB; instruction i, lane l copies LDS
+  // bytes 1024 i + 16 l (row rr, slot sl) from chunk sl ^ f(rr) of row rr.
+  const uint32_t lds_base = lds_offset(&lds[wave][0][0]);
+  const int last_slot = (kv_end - 1) & 15;
+  auto issue = [&](int t) {
+    const int32_t page = __builtin_amdgcn_readfirstlane(my_pages[t]);
+    const uint16_t* pbase = kvp + static_cast<int64_t>(page) * 16 * kMlaDk;
+    const int t0 = it.kv_begin + kMlaDecTileKeys * t;
+    const int valid_rows = kv_end - t0;  // >= 1
+    const uint32_t buf = lds_base + (t & 1) * kMlaPageBytes;
+#pragma unroll
+    for (int i = 0; i < kMlaPageDma; ++i) {
+      const int p = 1024 * i + 16 * lane;
+      int rr = p / kMlaRowBytes;
+      const int c = mla_slot(rr, (p % kMlaRowBytes) / 16);
+      if (rr >= valid_rows) rr = last_slot;  // past the keys: a valid key of this page
+      lds_dma16_sbase(static_cast<uint32_t>(rr * kMlaRowBytes + c * 16), pbase, buf + 1024 * i);
+    }
+  };
+
+  const int fk = (n16 >> 1) & 7;
+  const int k_off[2] = {n16 * kMlaRowBytes + 16 * ((0 + g4) ^ fk),
+                        n16 * kMlaRowBytes + 16 * ((4 + g4) ^ fk)};
+  // V^T of dim block b: rows 4 g4 + n16 / 4 (the 4 keys of this lane group),
+  // dims 16 b + 4 (n16 % 4) .. + 3
+  const int vr = 4 * g4 + (n16 >> 2);
+  const int fv = (vr >> 1) & 7;
+  const int vh = (n16 & 3) >> 1;
+  int v_off[4];
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4)
+    v_off[b4] = vr * kMlaRowBytes + 16 * ((2 * b4 + vh) ^ fv) + 8 * (n16 & 1);
+
+  float m = kNegInf;
+  float lsum = 0.0f;
+  f32x4 o[kMlaDv / 16];
+#pragma unroll
+  for (int b = 0; b < kMlaDv / 16; ++b) o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int t) {
+    const uint8_t* base = &lds[wave][t & 1][0];
+    constexpr int kAhead = 6, kRing = 8, kNs = kMlaDk / 32;
+    auto kfrag = [&](int s) -> bf16x8 {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(base + k_off[s & 1] + 128 * (s >> 1)));
+    };
+    f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 kf[kRing];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s) kf[s] = kfrag(s);
+#pragma unroll
+    for (int s = 0; s < kNs; ++s) {
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s % kRing], qf[s], sc, 0, 0, 0);
+      if (s + kAhead < kNs) kf[(s + kAhead) % kRing] = kfrag(s + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto vfrag = [&](int b) -> v4i16_t {
+      return __builtin_bit_cast(v4i16_t, lds_read_tr16(base + v_off[b & 3] + 128 * (b >> 2)));
+    };
+    v4i16_t vf[kRing];
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) vf[b] = vfrag(b);
+    const int t0 = it.kv_begin + kMlaDecTileKeys * t;
+    if (t0 + kMlaDecTileKeys - 1 > it.pos0) {  // a key past the row (decode: the last tile)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = (t0 + 4 * g4 + v <= pos) ? sc[v] : kNegInf;
+    }
+    if (!row_valid) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float mt = quad_max(mx) * scale_log2;
+    const bool raise = mt > m + kLazyMax;
+    const float m_new = raise ? mt : m;
+    const float alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+    float p[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[v] = fast_exp2(__builtin_fmaf(sc[v], scale_log2, neg_m));
+      psum += p[v];
+    }
+    const v4i16_t pw = __builtin_bit_cast(
+        v4i16_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+    if (__any(raise)) {
+      lsum *= alpha;
+#pragma unroll
+      for (int b = 0; b < kMlaDv / 16; ++b) o[b] *= alpha;
+    }
+    lsum += psum;
+    m = m_new;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b) {
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[b % kRing], pw, o[b], 0, 0, 0);
+      if (b + kAhead < kMlaDv / 16) vf[(b + kAhead) % kRing] = vfrag(b + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  issue(0);
+  if (n_tiles > 1) issue(1);
+  for (int t = 0; t < n_tiles; ++t) {
+    mla_dec_wait(t + 1 < n_tiles);  // this tile's DMAs have landed
+    compute(t);                     // its LDS reads are all complete when it returns
+    if (t + 2 < n_tiles) issue(t + 2);
+  }
+
+  const float l_row = quad_sum(lsum);
+  if (!row_valid) return;
+  float lse_nat = kNegInf;
+  float inv = 0.0f;
+  if (l_row > 0.0f) {
+    inv = 1.0f / l_row;
+    lse_nat = (m + fast_log2(l_row)) * kLn2;
+  }
+  if (it.state < 0) {
+    uint16_t* orow = out + row_idx * kMlaDv;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b)
+      *reinterpret_cast<uint2*>(orow + 16 * b + 4 * g4) =
+          make_uint2(pack_bf16x2(o[b][0] * inv, o[b][1] * inv),
+                     pack_bf16x2(o[b][2] * inv, o[b][3] * inv));
+    if (lse_out != nullptr && g4 == 0) lse_out[row_idx] = lse_nat;
+  } else {
+    const int64_t st = static_cast<int64_t>(it.state) + n16;
+    float* orow = o_part + st * kMlaDv;
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b)
+      *reinterpret_cast<float4*>(orow + 16 * b + 4 * g4) =
+          make_float4(o[b][0] * inv, o[b][1] * inv, o[b][2] * inv, o[b][3] * inv);
+    if (g4 == 0) lse_part[st] = lse_nat;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of a tile's partitions (prefill rows spanning several partitions,
 // decode requests longer than one partition): row x of MergeItem mi folds
 // slots state0 + k * stride + x, k ascending, with fold_state. D/4 threads
@@ -1711,10 +1912,18 @@ bia_status run_mla(const bia_plan* plan, bia_mode mode, const void* q, const voi
   auto* o = static_cast<uint16_t*>(out);
   int hb_shift = 0;
   while ((1 << hb_shift) < d.group) ++hb_shift;
-  hipLaunchKernelGGL(mla_kernel, dim3(L.n), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const WorkItem*>(L.items), static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(kv_pool), page_table_dev, sm_scale * kLog2e,
-                     d.num_qo_heads, hb_shift, d.split, o, lse, L.o_part, L.lse_part);
+  if (mode == BIA_MODE_DECODE && d.group <= 16 && d.split <= 16 * kMlaDecMaxPages) {
+    hipLaunchKernelGGL(mla_decode_kernel, dim3((L.n + 3) / 4), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const WorkItem*>(L.items), static_cast<int>(L.n),
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_pool),
+                       page_table_dev, sm_scale * kLog2e, d.num_qo_heads, d.group, d.split, o,
+                       lse, L.o_part, L.lse_part);
+  } else {
+    hipLaunchKernelGGL(mla_kernel, dim3(L.n), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const WorkItem*>(L.items), static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kv_pool), page_table_dev, sm_scale * kLog2e,
+                       d.num_qo_heads, hb_shift, d.split, o, lse, L.o_part, L.lse_part);
+  }
   if (!d.merges.empty()) {
     const ListLaunch M = plan_merges(d, ws);
     hipLaunchKernelGGL(merge_tiles_kernel<kMlaDv>, dim3(M.n), dim3(kThreads), 0, stream,
