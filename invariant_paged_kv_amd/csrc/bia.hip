@@ -289,13 +289,7 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int64_t q_off =
       (static_cast<int64_t>(it.q_row0 + tok) * num_qo_heads + it.kv_head * g + hj) * D;
 
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row_valid) w = *reinterpret_cast<const uint4*>(q + q_off + 16 * s + 8 * hi);
-    qf[s] = __builtin_bit_cast(bf16x8, w);
-  }
+  bf16x8 qf[D / 16];  // loaded after the first page ids (prologue)
 
   const int last = it.pos0 + it.n_tok - 1;
   const int kv_end = min(it.kv_begin + split, last + 1);
@@ -425,6 +419,16 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   f32x16 sacc[2];
   int32_t pg_v = pages(0);
   int32_t pg_k = pages(1);
+  // q after the page ids: the first DMAs wait only for the ids, and the q
+  // tile's latency overlaps theirs
+  // (rows past the tile's tokens read the tile's first token instead: an
+  // unconditional load, and those rows are never written)
+  const int64_t q_ld = row_valid ? q_off
+                                 : (static_cast<int64_t>(it.q_row0) * num_qo_heads +
+                                    it.kv_head * g + hj) * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + q_ld + 16 * s + 8 * hi));
   {
     const TilePages p0 = take_pages(pg_v);
     const TilePages p1 = take_pages(pg_k);
@@ -591,7 +595,17 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----
   const float l_row = lsum + __shfl_xor(lsum, 32);
-  if (!row_valid) return;
+  // The row's indices again, from a fresh lane id: kept live across the
+  // tile loop they would take registers the loop needs.
+  const int lane_e = static_cast<int>(
+      __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+  const int hi_e = lane_e >> 5;
+  const int x_e = wave * 32 + (lane_e & 31);
+  const int tok_e = x_e >> group_shift;
+  const int hj_e = x_e & (g - 1);
+  if (tok_e >= it.n_tok) return;
+  const int64_t q_off_e =
+      (static_cast<int64_t>(it.q_row0 + tok_e) * num_qo_heads + it.kv_head * g + hj_e) * D;
   float lse_nat = kNegInf;
   float inv = 0.0f;
   if (l_row > 0.0f) {
@@ -599,33 +613,33 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     lse_nat = (m + fast_log2(l_row)) * kLn2;
   }
   if (it.state < 0) {
-    uint16_t* orow = out + q_off;
+    uint16_t* orow = out + q_off_e;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int d = 32 * b + 8 * v4 + 4 * hi;
+        const int d = 32 * b + 8 * v4 + 4 * hi_e;
         const uint2 w = make_uint2(pack_bf16x2(o[b][4 * v4] * inv, o[b][4 * v4 + 1] * inv),
                                    pack_bf16x2(o[b][4 * v4 + 2] * inv, o[b][4 * v4 + 3] * inv));
         *reinterpret_cast<uint2*>(orow + d) = w;
       }
     }
-    if (lse_out != nullptr && hi == 0)
-      lse_out[static_cast<int64_t>(it.q_row0 + tok) * num_qo_heads + it.kv_head * g + hj] = lse_nat;
+    if (lse_out != nullptr && hi_e == 0)
+      lse_out[static_cast<int64_t>(it.q_row0 + tok_e) * num_qo_heads + it.kv_head * g + hj_e] = lse_nat;
   } else {
-    const int64_t st = static_cast<int64_t>(it.state) + x;
+    const int64_t st = static_cast<int64_t>(it.state) + x_e;
     float* orow = o_part + st * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int d = 32 * b + 8 * v4 + 4 * hi;
+        const int d = 32 * b + 8 * v4 + 4 * hi_e;
         *reinterpret_cast<float4*>(orow + d) =
             make_float4(o[b][4 * v4] * inv, o[b][4 * v4 + 1] * inv, o[b][4 * v4 + 2] * inv,
                         o[b][4 * v4 + 3] * inv);
       }
     }
-    if (hi == 0) lse_part[st] = lse_nat;
+    if (hi_e == 0) lse_part[st] = lse_nat;
   }
 }
 
