@@ -594,7 +594,13 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   }
 
   // ---- this partition's state for the row: o = O / l, lse = m + log l ----
-  const float l_row = lsum + __shfl_xor(lsum, 32);
+  // l: this lane's half plus lane ^ 32's (v_permlane32_swap hands each lane
+  // its own and its partner's value; the sum is the same in either order)
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, lsum),
+                                                    __builtin_bit_cast(unsigned, lsum), false,
+                                                    false);
+  const float l_row = __builtin_bit_cast(float, static_cast<unsigned>(lsw[0])) +
+                      __builtin_bit_cast(float, static_cast<unsigned>(lsw[1]));
   // The row's indices again, from a fresh lane id: kept live across the
   // tile loop they would take registers the loop needs.
   const int lane_e = static_cast<int>(
@@ -603,9 +609,6 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int x_e = wave * 32 + (lane_e & 31);
   const int tok_e = x_e >> group_shift;
   const int hj_e = x_e & (g - 1);
-  if (tok_e >= it.n_tok) return;
-  const int64_t q_off_e =
-      (static_cast<int64_t>(it.q_row0 + tok_e) * num_qo_heads + it.kv_head * g + hj_e) * D;
   float lse_nat = kNegInf;
   float inv = 0.0f;
   if (l_row > 0.0f) {
@@ -613,20 +616,50 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     lse_nat = (m + fast_log2(l_row)) * kLn2;
   }
   if (it.state < 0) {
-    uint16_t* orow = out + q_off_e;
+    // Whole rows out: the wave's 32 bf16 rows go to its quarter of the two K
+    // buffers (no wave reads them after the last tile's barrier), 16-byte
+    // chunk c of row r at slot c ^ (r % SLOTS); then each instruction stores
+    // 1 KB of whole rows (RB bytes per row), the rows of one token's heads
+    // being adjacent in `out`. One wave writes and reads its own region, so
+    // LDS order within the wave suffices.
+    uint8_t* stage = &lds[wave * 32 * RB];
+    const int r_e = lane_e & 31;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int d = 32 * b + 8 * v4 + 4 * hi_e;
-        const uint2 w = make_uint2(pack_bf16x2(o[b][4 * v4] * inv, o[b][4 * v4 + 1] * inv),
-                                   pack_bf16x2(o[b][4 * v4 + 2] * inv, o[b][4 * v4 + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + d) = w;
+        const int slot = (4 * b + v4) ^ (r_e & (SLOTS - 1));
+        *reinterpret_cast<uint2*>(stage + r_e * RB + slot * 16 + hi_e * 8) =
+            make_uint2(pack_bf16x2(o[b][4 * v4] * inv, o[b][4 * v4 + 1] * inv),
+                       pack_bf16x2(o[b][4 * v4 + 2] * inv, o[b][4 * v4 + 3] * inv));
       }
     }
-    if (lse_out != nullptr && hi_e == 0)
+    constexpr int kRowsPerStore = 1024 / RB;
+    constexpr int kStores = 32 / kRowsPerStore;
+    const int c = lane_e % SLOTS;
+    uint4 w[kStores];
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+      const int rr = i * kRowsPerStore + lane_e / SLOTS;
+      w[i] = *reinterpret_cast<const uint4*>(stage + rr * RB + (c ^ (rr & (SLOTS - 1))) * 16);
+    }
+    // all reads issued before the first store (else each is sunk into its
+    // store's branch and waited for alone)
+#pragma unroll
+    for (int i = 0; i < kStores; ++i)
+      asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+      const int xr = wave * 32 + i * kRowsPerStore + lane_e / SLOTS;
+      const int tr = xr >> group_shift;
+      if (tr < it.n_tok)
+        *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(it.q_row0 + tr) * num_qo_heads +
+                                         it.kv_head * g + (xr & (g - 1))) * D + c * 8) = w[i];
+    }
+    if (lse_out != nullptr && hi_e == 0 && tok_e < it.n_tok)
       lse_out[static_cast<int64_t>(it.q_row0 + tok_e) * num_qo_heads + it.kv_head * g + hj_e] = lse_nat;
   } else {
+    if (tok_e >= it.n_tok) return;
     const int64_t st = static_cast<int64_t>(it.state) + x_e;
     float* orow = o_part + st * D;
 #pragma unroll
