@@ -38,8 +38,9 @@
  * lse, workspace); the library owns the plan (host memory plus a pinned host
  * copy of its work list). Run calls are asynchronous on `stream` (a
  * hipStream_t; NULL means the null stream), never synchronise the host, and
- * copy the plan's work list into the head of the workspace with
- * hipMemcpyAsync, so the plan and the workspace must stay alive until the
+ * copy the plan's work list into the head of the workspace with a small
+ * kernel that reads the plan's pinned host copy, so the plan and the
+ * workspace must stay alive until the
  * stream has passed the call, and one workspace must not serve two calls that
  * can overlap.
  *

@@ -1761,18 +1761,36 @@ bia_status hip_fail(hipError_t e, const char* what) {
   return bia::fail(BIA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Pinned host copy of the plan's work list, made once per plan so the
-// per-run upload is a true async copy.
+// Pinned host copy of the plan's work list, made once per plan. It is
+// mapped and coherent (fine-grained): the upload kernel reads it over the
+// bus without caching, so a buffer that reuses freed pinned pages never
+// returns stale lines.
 bia_status ensure_pinned(const bia_plan* plan) {
   std::lock_guard<std::mutex> lock(g_pin_mutex);
   bia_plan* p = const_cast<bia_plan*>(plan);
   if (p->pinned != nullptr || p->d.blob_bytes == 0) return BIA_OK;
   void* h = nullptr;
-  hipError_t e = hipHostMalloc(&h, p->d.blob_bytes, hipHostMallocDefault);
+  hipError_t e = hipHostMalloc(&h, p->d.blob_bytes, hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work list)");
+  void* dptr = nullptr;
+  e = hipHostGetDevicePointer(&dptr, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return hip_fail(e, "hipHostGetDevicePointer(work list)");
+  }
   std::memcpy(h, p->d.blob.data(), p->d.blob_bytes);
   p->pinned = h;
+  p->pinned_dev = dptr;
   return BIA_OK;
+}
+
+// Work-list upload as a kernel on the run's stream (no copy-engine handoff
+// before the kernels that read it): 16-byte words, grid-stride.
+__global__ void __launch_bounds__(kThreads) upload_kernel(const uint4* __restrict__ src,
+                                                          uint4* __restrict__ dst, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    dst[i] = src[i];
 }
 
 int log2_exact(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
@@ -1803,9 +1821,19 @@ bia_status check_run(const bia_plan* plan, bia_mode mode, bool mla, const void* 
 bia_status upload(const bia_plan* plan, void* workspace, hipStream_t stream) {
   bia_status st = ensure_pinned(plan);
   if (st != BIA_OK) return st;
-  hipError_t e = hipMemcpyAsync(workspace, plan->pinned, plan->d.blob_bytes,
-                                hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  const size_t bytes = plan->d.blob_bytes;
+  if (bytes == 0) return BIA_OK;
+  if (bytes % 16 != 0) {  // every list entry is 16 or 32 bytes
+    hipError_t e = hipMemcpyAsync(workspace, plan->pinned, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+    return BIA_OK;
+  }
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
+  hipLaunchKernelGGL(upload_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(plan->pinned_dev), static_cast<uint4*>(workspace), n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "work-list upload launch");
   return BIA_OK;
 }
 

@@ -95,7 +95,8 @@ struct DecodeGraphData {
 // The opaque handles of the C ABI.
 struct bia_plan {
   bia::PlanData d;
-  void* pinned = nullptr;  // pinned copy of d.blob, made by the launch layer
+  void* pinned = nullptr;      // pinned copy of d.blob, made by the launch layer
+  void* pinned_dev = nullptr;  // the same memory as the device addresses it
 };
 
 struct bia_decode_graph {
