@@ -321,9 +321,9 @@ def main():
                          "records a plain copy of known size (HBM-byte calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one "
-              "GPU (one GPU's share of the attention at its real shape); run with "
-              "--gpus 1", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library runs on one "
+              "GPU and this benchmark measures that GPU's share of the attention at its "
+              "real shape; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
