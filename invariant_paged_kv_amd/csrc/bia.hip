@@ -681,10 +681,10 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 // `split` keys), g q heads. The partition's keys go in 16-key chunks to the 4
 // waves round-robin (chunk c -> wave c % 4). In a wave, 8 lanes share one key
 // (each holds D/8 of its dims, so 16-byte loads read whole rows) and a lane
-// group takes keys c*16 + ks and c*16 + 8 + ks (one page). Chunks are double
-// buffered in registers: the loads of a wave's next chunk are in flight
-// while the current one is computed, and page ids are read a chunk earlier
-// still.
+// group takes keys c*16 + ks and c*16 + 8 + ks (one page). Chunks rotate
+// through kDecodeBuffers (3) register buffers: the loads of a wave's next two
+// chunks are in flight while the current one is computed, and page ids are
+// read a chunk earlier still.
 //
 // Scores: v_dot2_f32_bf16 partial dots, reduced over the 8 lanes with three
 // DPP adds. PV: the two keys' probabilities (bf16) and the two keys' values
