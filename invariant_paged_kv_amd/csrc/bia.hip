@@ -136,13 +136,16 @@ __device__ __forceinline__ float fold_finish(float M, float sum, float (&acc)[N]
 //
 // Softmax bookkeeping, all per row and so independent of the tile holding
 // the row: the running max m is raised only when a tile's max exceeds it by
-// more than kLazyMax (base-2 units), so most tiles rescale nothing; scores
+// more than kLazyMax (base-2 units), so most tiles rescale nothing, and the
+// tile max is only taken when a lane's probability sum against the current m
+// exceeds 2^kLazyMax (or on the row's first tile with a visible key); scores
 // are scaled inside the exponent (exp2(s * c - m)); masking runs only on
 // tiles that reach past the wave's first row position (elsewhere every key
 // is visible to every row of the wave). The row sum adds the fp32
 // probabilities (summing their bf16 roundings would cost ~1e-3 in lse).
 // ---------------------------------------------------------------------------
 constexpr float kLazyMax = 8.0f;
+constexpr float kLazyP = 256.0f;  // 2^kLazyMax
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -284,6 +287,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   const int hj = x & (g - 1);
   const bool row_valid = tok < it.n_tok;
   const int pos = row_valid ? it.pos0 + tok : -1;
+  // the row has visible keys in this item's partition (its first tile holds one)
+  const bool row_live = pos >= it.kv_begin;
   // Position of the wave's first row: tiles ending at or before it need no mask.
   const int wave_pos0 = it.pos0 + ((wave * 32) >> group_shift);
   const int64_t q_off =
@@ -496,38 +501,24 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     }
 
     // ---- phase A ----
-    float mq[4];
-    float m_new = m, alpha = 1.0f, neg_m = 0.0f, psum = 0.0f;
-    bool raise = false;
+    // Probabilities against the running max as it stands, p = exp2(s c - m),
+    // one key pair per score MFMA. With the lazy max no p exceeds
+    // 2^kLazyMax unless the tile must raise m, and a lane's sum over its 32
+    // keys exceeds 2^kLazyMax whenever one of its p does; so the tile max is
+    // taken only when that sum (or a row with no max yet) asks for it.
+    const float neg_m = (m == kNegInf) ? 0.0f : -m;
+    float psum = 0.0f;
     uint32_t pw[16];  // packed bf16 probabilities, pair pi = 8 kb + (v / 2)
-    auto softmax_step = [&](int i) {
-      if (i < 4) {
-        const int kbk = i >> 1, v0 = 8 * (i & 1);
-        float x = cur[kbk][v0];
-#pragma unroll
-        for (int v = 1; v < 8; ++v) x = fmaxf(x, cur[kbk][v0 + v]);
-        mq[i] = x;
-      } else if (i == 4) {
-        const float mt = max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * scale_log2;
-        raise = mt > m + kLazyMax;  // true on the first tile with a visible key
-        m_new = raise ? mt : m;
-        alpha = raise ? fast_exp2(m - m_new) : 1.0f;
-        neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-      } else if (i < 13) {
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const int pi = 2 * (i - 5) + q2;
-          const int kbk = pi >> 3, v = 2 * (pi & 7);
-          const float p0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m));
-          const float p1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m));
-          psum += p0;
-          psum += p1;
-          pw[pi] = pack_bf16x2(p0, p1);
-          // keep this step's results here: without it the compiler sinks
-          // them past the rescale branch, out of the interleave
-          asm volatile("" : "+v"(pw[pi]), "+v"(psum));
-        }
-      }
+    auto softmax_step = [&](int pi) {
+      const int kbk = pi >> 3, v = 2 * (pi & 7);
+      const float p0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m));
+      const float p1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m));
+      psum += p0;
+      psum += p1;
+      pw[pi] = pack_bf16x2(p0, p1);
+      // keep this step's results here: without it the compiler sinks them
+      // past the raise branch, out of the interleave
+      asm volatile("" : "+v"(pw[pi]), "+v"(psum));
     };
     if constexpr (kHasNext) {
       nxt[0] = f32x16{};
@@ -549,10 +540,47 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 16; ++i) softmax_step(i);
     }
-    if (__any(raise)) {  // lanes that did not raise have alpha == 1 exactly
-      lsum *= alpha;
+
+    // Raise test, per row. A row asks for it when either half's sum exceeds
+    // 2^kLazyMax or it has visible keys in this partition and no max yet;
+    // then it raises iff the tile max exceeds m by more than kLazyMax, and a
+    // raised row recomputes its p. A row that does not raise keeps the p
+    // above and alpha == 1 exactly, so its bits never depend on the other
+    // rows of the wave.
+    const bool ask = (psum > kLazyP) || (m == kNegInf && row_live);
+    bool raise = false;
+    float m_new = m, alpha = 1.0f;
+    if (__any(ask)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(ask),
+                                                       static_cast<unsigned>(ask), false, false);
+      const bool ask_row = (static_cast<unsigned>(sw[0]) | static_cast<unsigned>(sw[1])) != 0u;
+      float x = cur[0][0];
 #pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x = fmaxf(x, cur[kbk][v]);
+      const float mt = max_halves(x) * scale_log2;
+      raise = ask_row && mt > m + kLazyMax;  // true on a row's first tile with a visible key
+      m_new = raise ? mt : m;
+      alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+      if (__any(raise)) {
+        const float neg_m2 = -m_new;  // finite wherever it is used (raise)
+        float ps2 = 0.0f;
+#pragma unroll
+        for (int pi = 0; pi < 16; ++pi) {
+          const int kbk = pi >> 3, v = 2 * (pi & 7);
+          const float p0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m2));
+          const float p1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m2));
+          ps2 += p0;
+          ps2 += p1;
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pw[pi] = raise ? w : pw[pi];
+        }
+        psum = raise ? ps2 : psum;
+        lsum *= alpha;  // lanes that did not raise have alpha == 1 exactly
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      }
     }
     lsum += psum;
     m = m_new;
