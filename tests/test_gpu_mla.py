@@ -223,3 +223,21 @@ def test_mla_rejects_wrong_shapes():
         bia.bia_prefill_paged(plan, b.q, b.k_pool, b.k_pool, page_table_dev(b), b.sm_scale,
                               out, lse, ws)
     plan.close()
+
+
+@pytest.mark.parametrize("hq", [16, 128])
+def test_mla_rising_logits(hq):
+    """Latent logits that climb along the sequence: rows raise their running
+    max mid-row again and again; the 1500-key request spans partitions whose
+    states merge with very different lse. Decode covers the one-wave kernel
+    (16 heads) and the 64-row kernel (128 heads)."""
+    say(f"mla rising logits hq={hq}")
+    b = W.rising_mla_batch([400, 200, 9], [400, 1500, 9], num_qo_heads=hq, seed=91,
+                           num_pages=256, rise=1.5, device=DEV)
+    out, lse = run_mla(b, split=256)
+    mla_parity(b, out, lse, f"mla rising prefill hq={hq}")
+    ctx = [1, 300, 2048, 2049, 4000]
+    d = W.rising_mla_batch([1] * len(ctx), ctx, num_qo_heads=hq, seed=92, num_pages=1024,
+                           rise=1.5, device=DEV)
+    out, lse = run_mla(d, mode=bia.BIA_MODE_DECODE)
+    mla_parity(d, out, lse, f"mla rising decode hq={hq}")

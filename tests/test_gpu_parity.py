@@ -162,3 +162,25 @@ def test_merge_states(D):
     assert np.max(np.abs(l[fin] - rl[fin])) <= LSE_TOL
     # a row with one live state reproduces it exactly
     assert bits_equal(out[1].cpu(), v[indptr[1]].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("split", [256, 4096])
+def test_rising_logits_prefill(split):
+    """Logits that climb along the sequence make a row's running max rise
+    again and again (many raises after the first tile, with O and l already
+    holding earlier keys); the partitions of the 4500-key request merge states
+    whose lse differ by tens of units."""
+    say(f"rising logits prefill, split {split}")
+    b = W.rising_batch([1000, 300, 37], [1000, 4500, 37], seed=61, num_pages=512,
+                       device=DEV, **W.QWEN3_8B)
+    out, lse = run_prefill(b, split=split)
+    assert_parity(out, lse, b, what=f"rising prefill split {split}")
+
+
+def test_rising_logits_decode():
+    say("rising logits decode")
+    ctx = [1, 100, 2048, 2049, 5000, 9000]
+    b = W.rising_batch([1] * len(ctx), ctx, seed=62, num_pages=2048, device=DEV,
+                       **W.QWEN3_8B)
+    out, lse = run_decode(b)
+    assert_parity(out, lse, b, what="rising decode")

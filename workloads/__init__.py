@@ -242,6 +242,29 @@ def make_mla_batch(requests: Sequence[Request], *, num_qo_heads: int, num_pages:
     return b
 
 
+def rising_mla_batch(qo_lens, kv_lens, *, num_qo_heads: int, seed: int, num_pages: int,
+                     rise: float = 3.0, device="cpu") -> PagedBatch:
+    """Latent-cache batch whose logits climb along the sequence (the latent
+    analogue of ``rising_batch``): latent row j of a request = (rise j /
+    kv_len) + N(0, 0.25^2) per dim, q = 1 + N(0, 0.5^2), one PCG64 stream per
+    request; about 0.19 base-2 units per key at kv_len 1000 with the default
+    scale 1 / sqrt(192)."""
+    kvs, qs = [], []
+    for r, (qo, kv) in enumerate(zip(qo_lens, kv_lens)):
+        g = np.random.Generator(np.random.PCG64(seed * 1013 + r))
+        ramp = (rise * np.arange(kv, dtype=np.float32) / max(kv, 1))[:, None, None]
+        kvs.append(torch.from_numpy(
+            (ramp + 0.25 * g.standard_normal((kv, 1, MLA_DK), dtype=np.float32)).astype(np.float32)))
+        qs.append(torch.from_numpy(
+            (1.0 + 0.5 * g.standard_normal((qo, num_qo_heads, MLA_DK), dtype=np.float32))
+            .astype(np.float32)))
+    b = assemble_batch(qo_lens, kv_lens, qs, kvs, kvs, num_pages=num_pages, batch_seed=seed,
+                       sm_scale=1.0 / math.sqrt(192.0), device=device)
+    b.v_pool = b.k_pool[..., :MLA_DV]
+    b.requests = [Request(qo, kv, seed * 1013 + r) for r, (qo, kv) in enumerate(zip(qo_lens, kv_lens))]
+    return b
+
+
 @dataclass
 class Sequence1:
     """One long request stored once in a pool, viewed as chunked calls.
@@ -298,6 +321,33 @@ def tiny_sequence(device="cpu") -> Sequence1:
     b = make_batch([Request(300, 300, 102)], num_pages=64, batch_seed=1,
                    device=device, keep_seq=True, **TINY)
     return Sequence1(b, 300)
+
+
+def rising_batch(qo_lens, kv_lens, *, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, seed: int, num_pages: int, rise: float = 6.0,
+                 device="cpu") -> PagedBatch:
+    """Keys whose logits climb along the sequence, so that a query's running
+    max keeps rising by many base-2 units as its keys are visited.
+
+    q = 1 + N(0, 0.5^2) per element, key j of a request = (rise j / kv_len) + N(0,
+    0.25^2) per element, v ~ N(0, 1), all drawn from one PCG64 stream per
+    request. With the 1/sqrt(D) scale a query's logit grows by about
+    rise * D / sqrt(D) * log2(e) / kv_len base-2 units per key (about 0.1 at
+    D = 128, kv_len 1000, rise 6)."""
+    qs, ks, vs = [], [], []
+    for r, (qo, kv) in enumerate(zip(qo_lens, kv_lens)):
+        g = np.random.Generator(np.random.PCG64(seed * 1009 + r))
+        ramp = (rise * np.arange(kv, dtype=np.float32) / max(kv, 1))[:, None, None]
+        ks.append(torch.from_numpy(
+            (ramp + 0.25 * g.standard_normal((kv, num_kv_heads, head_dim), dtype=np.float32))
+            .astype(np.float32)))
+        vs.append(torch.from_numpy(g.standard_normal((kv, num_kv_heads, head_dim),
+                                                     dtype=np.float32)))
+        qs.append(torch.from_numpy(
+            (1.0 + 0.5 * g.standard_normal((qo, num_qo_heads, head_dim), dtype=np.float32))
+            .astype(np.float32)))
+    return assemble_batch(qo_lens, kv_lens, qs, ks, vs, num_pages=num_pages,
+                          batch_seed=seed, device=device)
 
 
 def qwen_prefill(device="cpu", batch=8, length=4096, num_pages=65536, seed=2):
