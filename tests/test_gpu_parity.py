@@ -164,15 +164,17 @@ def test_merge_states(D):
     assert bits_equal(out[1].cpu(), v[indptr[1]].to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("heads", [W.QWEN3_8B, dict(num_qo_heads=4, num_kv_heads=1, head_dim=64)],
+                         ids=["hq32_hkv8_d128", "hq4_hkv1_d64"])
 @pytest.mark.parametrize("split", [256, 4096])
-def test_rising_logits_prefill(split):
+def test_rising_logits_prefill(split, heads):
     """Logits that climb along the sequence make a row's running max rise
     again and again (many raises after the first tile, with O and l already
     holding earlier keys); the partitions of the 4500-key request merge states
     whose lse differ by tens of units."""
-    say(f"rising logits prefill, split {split}")
+    say(f"rising logits prefill, split {split}, {heads}")
     b = W.rising_batch([1000, 300, 37], [1000, 4500, 37], seed=61, num_pages=512,
-                       device=DEV, **W.QWEN3_8B)
+                       device=DEV, **heads)
     out, lse = run_prefill(b, split=split)
     assert_parity(out, lse, b, what=f"rising prefill split {split}")
 
