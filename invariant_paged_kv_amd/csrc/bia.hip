@@ -113,10 +113,12 @@ __device__ __forceinline__ float fold_finish(float M, float sum, float (&acc)[N]
 // K and V reach LDS by DMA (global_load_lds_dwordx4: 16 bytes per lane from
 // the lane's own global address into LDS at M0 + 16 * lane, checked on the
 // GPU with an in-bounds probe), so no registers stage them. Two buffers each
-// for K and V; per tile: wait for this wave's DMAs, one barrier, then issue
-// the DMAs of K(j+2) and V(j+1) into the buffers the previous tile finished
-// with, then the score MFMAs of tile j+1 overlapped with the softmax of tile
-// j, then PV of tile j. The DMAs are inline asm with an explicit wait, so the
+// for K and V; per tile: wait for this wave's DMAs, one barrier, then the
+// DMAs of K(j+2) and V(j+1) into the buffers the previous tile finished with
+// (each wave issues its share after a different score MFMA, so the four
+// waves' bursts do not queue behind each other), the score MFMAs of tile j+1
+// overlapped with the softmax of tile j, then PV of tile j. The DMAs are
+// inline asm with an explicit wait, so the
 // compiler does not make every later LDS read wait for all outstanding loads.
 //
 // LDS rows are 2D bytes, unpadded (a DMA instruction fills 1 KB
@@ -451,11 +453,22 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
   // j+1 (into nxt) overlapped with the softmax of tile j (cur), PV of tile j.
   // P is the parity of j (K(j+1) is in buffer 1 - P, V(j) in buffer 2 + P).
   // K fragment of score MFMA i (head-dim step i / 2, key block i % 2).
+  // Per-lane offsets of K step s = 2 a + c: kbase[c] ^ 64 a, since chunk
+  // (2 s + hi) ^ swz = (4 a) ^ ((2 c + hi) ^ swz); of the V^T reads of d block
+  // b: vbase[e2] ^ 64 b, since (4 b + v_lo) ^ swz = (4 b) ^ (v_lo ^ swz). Two
+  // registers each instead of eight; bits 6-7 of these offsets hold nothing
+  // else (row * RB is a multiple of 256, v_byte is 0 or 8).
+  uint32_t kbase[2], vbase[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    kbase[c2] = static_cast<uint32_t>(col * RB + (((2 * c2 + hi) ^ k_sw) * 16));
+    vbase[c2] = static_cast<uint32_t>(v_row_off[c2] + ((v_lo ^ v_sw[c2]) * 16));
+  }
   auto kfrag = [&](int buf, int i) -> bf16x8 {
-    const int slot = (2 * (i >> 1) + hi) ^ k_sw;
+    const int s2 = i >> 1;
+    const uint32_t off = kbase[s2 & 1] ^ static_cast<uint32_t>(64 * (s2 >> 1));
     return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(&lds[buf * TB + (32 * (i & 1) + col) * RB +
-                                                     slot * 16]));
+        bf16x8, *reinterpret_cast<const uint4*>(&lds[buf * TB + (32 * (i & 1)) * RB + off]));
   };
   // V^T fragment of PV MFMA i: key block kb = i / (2 DB), half h = (i / DB) % 2,
   // dim block b = i % DB (so consecutive MFMAs accumulate into different o[b]).
@@ -464,8 +477,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     const int kbk = i / (2 * DB);
     const int h = (i / DB) & 1;
     const uint8_t* rb = &lds[buf * TB + (32 * kbk + 16 * h) * RB];
-    const uint2 lo = lds_read_tr16(rb + v_row_off[0] + ((4 * b + v_lo) ^ v_sw[0]) * 16);
-    const uint2 up = lds_read_tr16(rb + v_row_off[1] + ((4 * b + v_lo) ^ v_sw[1]) * 16);
+    const uint2 lo = lds_read_tr16(rb + (vbase[0] ^ static_cast<uint32_t>(64 * b)));
+    const uint2 up = lds_read_tr16(rb + (vbase[1] ^ static_cast<uint32_t>(64 * b)));
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, up.x, up.y));
   };
 
@@ -480,14 +493,40 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     constexpr int P = decltype(parity)::value;
     wait_dma();
     __syncthreads();  // K(j+1), V(j) are in LDS; every wave is done with tile j-1
+    // the derived offsets are recomputed per tile rather than kept live
+    // (kept live, they and the page ids below push the loop into spills)
+    asm volatile("" : "+v"(kbase[0]), "+v"(kbase[1]), "+v"(vbase[0]), "+v"(vbase[1]));
+    // Page ids right after the barrier. For whole tiles (K(j+2) whole implies
+    // V(j+1) whole) the DMAs go out later, after score MFMA wave * D / 32 of
+    // phase A, so the four waves' bursts reach the address path one after
+    // another instead of all right after the barrier; each wave then needs
+    // only its own page of each tile. Ragged tiles go out at once.
+    bool stagger = false;
+    int32_t own_k = 0, own_v = 0;
     if constexpr (kHasNext) {
-      const TilePages kpg = take_pages(pg_k);
-      const TilePages vpg = take_pages(pg_v);
-      if (j + 2 < n_tiles) issue(kp, j + 2, P, kpg);
-      issue(vp, j + 1, 3 - P, vpg);
+      stagger = it.kv_begin + 64 * (j + 3) <= kv_end;
+      if (stagger) {
+        own_k = __builtin_amdgcn_readlane(pg_k, wave);
+        own_v = __builtin_amdgcn_readlane(pg_v, wave);
+        asm volatile("" : "+s"(own_k), "+s"(own_v));
+      } else {
+        const TilePages kpg = take_pages(pg_k);
+        const TilePages vpg = take_pages(pg_v);
+        if (j + 2 < n_tiles) issue(kp, j + 2, P, kpg);
+        issue(vp, j + 1, 3 - P, vpg);
+      }
       pg_v = pg_k;
       pg_k = pages(j + 3);
     }
+    auto dmas = [&]() {
+      if (!stagger) return;
+      dma_page<IPW>(dma_off,
+                    reinterpret_cast<uint64_t>(kp + static_cast<int64_t>(own_k) * 16 * slot_stride),
+                    lds_base + P * TB + wave * 16 * RB);
+      dma_page<IPW>(dma_off,
+                    reinterpret_cast<uint64_t>(vp + static_cast<int64_t>(own_v) * 16 * slot_stride),
+                    lds_base + (3 - P) * TB + wave * 16 * RB);
+    };
     const int t0 = it.kv_begin + 64 * j;
     if (t0 + 63 > wave_pos0) {  // wave-uniform: some key is past some row
 #pragma unroll
@@ -532,6 +571,7 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
                                                              0, 0, 0);
         if (i + 2 < D / 8) kf[(i + 2) % 3] = kfrag(1 - P, i + 2);
         if (i < 16) softmax_step(i);
+        if (i % (D / 32) == 0 && i / (D / 32) == wave) dmas();  // slot wave * D / 32
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
