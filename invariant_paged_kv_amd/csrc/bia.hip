@@ -1683,8 +1683,8 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 //
 // Launch order (what the host planner's longest-first sort gives, computed
 // from kv_indptr alone by every workgroup): first the whole partitions of all
-// requests, partition-major, then each request's partial last partition, then
-// the empty slots (n_tok = 0: the decode kernel returns at once). Item index =
+// requests, partition-major, then the requests' partial last partitions,
+// longest first (ties by request index), then the empty slots (n_tok = 0: the decode kernel returns at once). Item index =
 // unit * Hkv + h, so consecutive workgroups, which the dispatcher deals
 // round-robin over the XCDs, are different kv heads of one (request,
 // partition); with (request, head, partition) order the XCD would follow the
@@ -1723,8 +1723,17 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
       np = len % split != 0 ? 1 : 0;
     }
   };
+  // 64-key tiles of request q's partial partition (0 when its slot holds the
+  // empty state of an invalid request): partial partitions go longest first
+  auto partial_tiles = [&](int q) -> int64_t {
+    const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
+    if (len < 1 || len > max_kv_len) return 0;
+    return (len % split + 63) / 64;
+  };
+  const int64_t my_tiles = partial_tiles(r);
   // integer sums over the requests (exact in any order): pages before r, whole
-  // partitions of all, partial partitions of all and of those before r
+  // partitions of all, partial partitions of all and of those launched before
+  // r's (more tiles, or as many and an earlier request)
   int64_t pages_before = 0, all_nf = 0, all_np = 0, np_before = 0;
   for (int q = tid; q < batch; q += kThreads) {
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
@@ -1732,9 +1741,10 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
     reserve(q, nf, np);
     all_nf += nf;
     all_np += np;
-    if (q < r) {
-      pages_before += len > 0 ? (len + 15) / 16 : 0;
-      np_before += np;
+    if (q < r) pages_before += len > 0 ? (len + 15) / 16 : 0;
+    if (np != 0) {
+      const int64_t tq = partial_tiles(q);
+      if (tq > my_tiles || (tq == my_tiles && q < r)) np_before += 1;
     }
   }
   sm_red[0][tid] = pages_before;

@@ -176,3 +176,6 @@ def test_device_plan_matches_host_plan():
     lens = np.minimum(live[:, 3] - live[:, 6], 2048)
     whole = lens == 2048
     assert not whole[np.argmax(~whole):].any() if (~whole).any() else True
+    # partial partitions longest first (in 64-key tiles), as the host plan sorts them
+    tiles = (lens[~whole] + 63) // 64
+    assert (np.diff(tiles) <= 0).all(), "partial partitions are not launched longest first"
