@@ -548,16 +548,23 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
     const float neg_m = (m == kNegInf) ? 0.0f : -m;
     float psum = 0.0f;
     uint32_t pw[16];  // packed bf16 probabilities, pair pi = 8 kb + (v / 2)
+    // Software-pipelined by one pair: step pi takes the exponentials of pair
+    // pi and sums and packs pair pi - 1, so no step waits on its own exp2
+    // results. Step 16 only finishes pair 15. Same operations, same order.
+    float e0 = 0.0f, e1 = 0.0f;
     auto softmax_step = [&](int pi) {
-      const int kbk = pi >> 3, v = 2 * (pi & 7);
-      const float p0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m));
-      const float p1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m));
-      psum += p0;
-      psum += p1;
-      pw[pi] = pack_bf16x2(p0, p1);
-      // keep this step's results here: without it the compiler sinks them
-      // past the raise branch, out of the interleave
-      asm volatile("" : "+v"(pw[pi]), "+v"(psum));
+      if (pi > 0) {
+        psum += e0;
+        psum += e1;
+        pw[pi - 1] = pack_bf16x2(e0, e1);
+        asm volatile("" : "+v"(pw[pi - 1]), "+v"(psum));
+      }
+      if (pi < 16) {
+        const int kbk = pi >> 3, v = 2 * (pi & 7);
+        e0 = fast_exp2(__builtin_fmaf(cur[kbk][v], scale_log2, neg_m));
+        e1 = fast_exp2(__builtin_fmaf(cur[kbk][v + 1], scale_log2, neg_m));
+        asm volatile("" : "+v"(e0), "+v"(e1));
+      }
     };
     if constexpr (kHasNext) {
       nxt[0] = f32x16{};
@@ -575,10 +582,10 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = D / 8; i < 16; ++i) softmax_step(i);
+      for (int i = D / 8; i <= 16; ++i) softmax_step(i);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) softmax_step(i);
+      for (int i = 0; i <= 16; ++i) softmax_step(i);
     }
 
     // Raise test, per row. A row asks for it when either half's sum exceeds
