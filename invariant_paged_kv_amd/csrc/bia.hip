@@ -1707,6 +1707,7 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 constexpr int32_t kGraphBadKvLen = 1;  // kv_len < 1 or > max_kv_len
 constexpr int32_t kGraphBadTable = 2;  // pages past page_table_capacity
 constexpr int32_t kGraphBadPage = 4;   // a page id outside [0, num_pages)
+constexpr int kGraphStagedBatch = 8192;  // requests whose partition counts the planner keeps in LDS
 
 __global__ void __launch_bounds__(kThreads)
 decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
@@ -1716,18 +1717,22 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
                          WorkItem* __restrict__ items, MergeItem* __restrict__ merges) {
   __shared__ int64_t sm_red[4][kThreads];
   __shared__ int32_t sm_bad;
+  __shared__ int32_t sm_nf[kGraphStagedBatch];
   const int r = blockIdx.x;
   const int batch = gridDim.x;
   const int tid = threadIdx.x;
-  // slots request q reserves: nf whole partitions and np (0 or 1) partial one
+  // slots request q reserves: nf whole partitions and np (0 or 1) partial one.
+  // A valid kv_len fits 32 bits; 32-bit division is a few instructions where
+  // the 64-bit one is a long software sequence
   auto reserve = [&](int q, int32_t& nf, int32_t& np) {
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
     if (len < 1 || len > max_kv_len) {
       nf = 0;
       np = 1;
     } else {
-      nf = static_cast<int32_t>(len / split);
-      np = len % split != 0 ? 1 : 0;
+      const int32_t l = static_cast<int32_t>(len);
+      nf = l / split;
+      np = l - nf * split != 0 ? 1 : 0;
     }
   };
   // 64-key tiles of request q's partial partition (0 when its slot holds the
@@ -1735,7 +1740,8 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   auto partial_tiles = [&](int q) -> int64_t {
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
     if (len < 1 || len > max_kv_len) return 0;
-    return (len % split + 63) / 64;
+    const int32_t l = static_cast<int32_t>(len);
+    return (l - (l / split) * split + 63) / 64;
   };
   const int64_t my_tiles = partial_tiles(r);
   // integer sums over the requests (exact in any order): pages before r, whole
@@ -1746,6 +1752,7 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
     int32_t nf, np;
     reserve(q, nf, np);
+    if (batch <= kGraphStagedBatch) sm_nf[q] = nf;  // read batch times per partition below
     all_nf += nf;
     all_np += np;
     if (q < r) pages_before += len > 0 ? (len + 15) / 16 : 0;
@@ -1779,6 +1786,8 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   if (!bad && page_off + n_pages > page_table_capacity) bad = kGraphBadTable;
   if (!bad) {
     bool any = false;
+    // unrolled so that a long request's page-id loads are in flight together
+#pragma unroll 8
     for (int64_t i = tid; i < n_pages; i += kThreads) {
       const int32_t pid = page_table[page_off + i];
       any = any || pid < 0 || pid >= num_pages;
@@ -1800,7 +1809,11 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
       unit = 0;
       for (int q = 0; q < batch; ++q) {
         int32_t nf, np;
-        reserve(q, nf, np);
+        if (batch <= kGraphStagedBatch) {
+          nf = sm_nf[q];
+        } else {
+          reserve(q, nf, np);
+        }
         unit += min(nf, sp) + (q < r && nf > sp ? 1 : 0);
       }
     } else {
