@@ -36,13 +36,15 @@
  *
  * Ownership: the caller owns every device buffer (q, pools, page table, out,
  * lse, workspace); the library owns the plan (host memory plus a pinned host
- * copy of its work list). Run calls are asynchronous on `stream` (a
- * hipStream_t; NULL means the null stream), never synchronise the host, and
+ * copy of its work list, a block drawn from a library-owned pool when the
+ * plan is made). Run calls are asynchronous on `stream` (a hipStream_t; NULL
+ * means the null stream), allocate nothing, never synchronise the host, and
  * copy the plan's work list into the head of the workspace with a small
- * kernel that reads the plan's pinned host copy, so the plan and the
- * workspace must stay alive until the
- * stream has passed the call, and one workspace must not serve two calls that
- * can overlap.
+ * kernel that reads the plan's pinned block. The workspace must stay alive
+ * until the stream has passed the call, and one workspace must not serve two
+ * calls that can overlap. The plan may be destroyed as soon as the run calls
+ * have returned: its pinned block goes back to the pool and is handed out
+ * again only after the device has passed every upload that read it.
  *
  * Errors: every call returns a bia_status; nothing is thrown across the ABI.
  * Arguments are checked before anything is enqueued. bia_last_error() gives a
@@ -120,7 +122,10 @@ typedef struct bia_plan bia_plan; /* opaque, library-owned */
  *       32, 64 or 128 (the one cached head is shared by every q head).
  * On success *out_plan receives a plan to free with bia_plan_destroy. The
  * arrays are not retained. batch == 0 gives an empty plan whose runs do
- * nothing.
+ * nothing. The pinned copy of the work list is taken here (from the pool, or
+ * newly pinned with hipHostMalloc when no free block is large enough), so
+ * run calls allocate nothing. In a process that sees no GPU the plan is made
+ * without it: it can be inspected, and a run returns BIA_ERR_HIP.
  */
 bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
                            const int32_t* kv_indptr, const int32_t* page_table,
@@ -133,8 +138,10 @@ bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
 /* Bytes of device workspace a run of this plan needs (0 for NULL). */
 size_t bia_plan_workspace_bytes(const bia_plan* plan);
 
-/* Free a plan. Only once every run enqueued with it has completed. NULL is a
- * no-op. */
+/* Free a plan. Allowed as soon as the run calls made with it have returned,
+ * also while their work is still queued: the pinned block goes back to the
+ * library's pool without being freed and without waiting for the device.
+ * NULL is a no-op. */
 void bia_plan_destroy(bia_plan* plan);
 
 /*

@@ -126,8 +126,9 @@ def _ptr_i32(a: np.ndarray):
 
 class Plan:
     """A library-owned plan (``bia_plan*``) plus the sizes needed to check the
-    tensors of its runs. Destroy it (``close()``, or let it be collected)
-    only after every run enqueued with it has completed."""
+    tensors of its runs. It may be destroyed (``close()``, or collected) as
+    soon as its run calls have returned; the library reuses its pinned
+    work-list block only after the device has read it."""
 
     def __init__(self, handle, mode, batch, num_qo_heads, num_kv_heads, head_dim,
                  num_pages, total_q, total_pages, split_size, flags=0):

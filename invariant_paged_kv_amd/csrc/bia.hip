@@ -27,6 +27,9 @@
 #include <cstring>
 #include <cstdint>
 #include <mutex>
+#include <new>
+#include <vector>
+#include <algorithm>
 #include <type_traits>
 
 #include "bia.h"
@@ -1853,33 +1856,115 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
 // ---------------------------------------------------------------------------
 // Launch layer.
 // ---------------------------------------------------------------------------
-std::mutex g_pin_mutex;
-
 bia_status hip_fail(hipError_t e, const char* what) {
   return bia::fail(BIA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Pinned host copy of the plan's work list, made once per plan. It is
-// mapped and coherent (fine-grained): the upload kernel reads it over the
-// bus without caching, so a buffer that reuses freed pinned pages never
-// returns stale lines.
-bia_status ensure_pinned(const bia_plan* plan) {
-  std::lock_guard<std::mutex> lock(g_pin_mutex);
-  bia_plan* p = const_cast<bia_plan*>(plan);
-  if (p->pinned != nullptr || p->d.blob_bytes == 0) return BIA_OK;
-  void* h = nullptr;
-  hipError_t e = hipHostMalloc(&h, p->d.blob_bytes, hipHostMallocMapped | hipHostMallocCoherent);
-  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work list)");
-  void* dptr = nullptr;
-  e = hipHostGetDevicePointer(&dptr, h, 0);
-  if (e != hipSuccess) {
-    (void)hipHostFree(h);
-    return hip_fail(e, "hipHostGetDevicePointer(work list)");
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Pinned work-list blocks. A plan takes one block from this library-owned
+// pool when it is made and gives it back when it is destroyed, so run calls
+// allocate nothing and destroying a plan never waits for the device. Each
+// block is mapped and coherent (the upload kernel reads it over the bus
+// without caching, so a reused block never returns stale lines) and carries
+// an event recorded on the run's stream right after the upload that reads
+// it: a returned block is handed out again only once that event has
+// completed, i.e. once the device has passed every upload that read it.
+// Blocks are never freed before the process ends (hipHostFree would
+// synchronise the device).
+// ---------------------------------------------------------------------------
+struct bia::PinBlock {
+  void* host = nullptr;
+  void* dev = nullptr;            // the same memory as the device addresses it
+  size_t bytes = 0;               // capacity (a power of two)
+  hipEvent_t done = nullptr;      // recorded after each upload from the block
+  hipStream_t last_stream = nullptr;
+  bool recorded = false;
+};
+
+namespace {
+
+struct PinPool {
+  std::mutex mu;
+  std::vector<bia::PinBlock*> free_blocks;  // ready to hand out
+  std::vector<bia::PinBlock*> returned;     // given back; may still be read
+};
+PinPool g_pin_pool;
+
+constexpr size_t kPinMinBytes = 4096;
+
+// Moves returned blocks whose last upload has completed to the free list
+// (hipEventQuery does not wait). Caller holds the pool's mutex.
+void pin_reclaim(PinPool& pool) {
+  size_t keep = 0;
+  for (size_t i = 0; i < pool.returned.size(); ++i) {
+    bia::PinBlock* b = pool.returned[i];
+    if (!b->recorded || hipEventQuery(b->done) == hipSuccess) {
+      b->recorded = false;
+      b->last_stream = nullptr;
+      pool.free_blocks.push_back(b);
+    } else {
+      pool.returned[keep++] = b;
+    }
   }
-  std::memcpy(h, p->d.blob.data(), p->d.blob_bytes);
-  p->pinned = h;
-  p->pinned_dev = dptr;
+  pool.returned.resize(keep);
+}
+
+// A block of at least `bytes`, from the pool or newly pinned.
+bia_status pin_acquire(size_t bytes, bia::PinBlock** out) {
+  *out = nullptr;
+  size_t cap = kPinMinBytes;
+  while (cap < bytes) cap <<= 1;
+  {
+    std::lock_guard<std::mutex> lock(g_pin_pool.mu);
+    pin_reclaim(g_pin_pool);
+    bia::PinBlock* best = nullptr;
+    size_t best_i = 0;
+    for (size_t i = 0; i < g_pin_pool.free_blocks.size(); ++i) {
+      bia::PinBlock* b = g_pin_pool.free_blocks[i];
+      if (b->bytes >= cap && (best == nullptr || b->bytes < best->bytes)) {
+        best = b;
+        best_i = i;
+      }
+    }
+    if (best != nullptr) {
+      g_pin_pool.free_blocks.erase(g_pin_pool.free_blocks.begin() + best_i);
+      *out = best;
+      return BIA_OK;
+    }
+  }
+  auto* b = new (std::nothrow) bia::PinBlock();
+  if (b == nullptr) return bia::fail(BIA_ERR_INVALID_ARG, "out of host memory");
+  hipError_t e = hipHostMalloc(&b->host, cap,
+                               hipHostMallocMapped | hipHostMallocCoherent |
+                                   hipHostMallocPortable);
+  if (e != hipSuccess) {
+    delete b;
+    return hip_fail(e, "hipHostMalloc(work list)");
+  }
+  e = hipHostGetDevicePointer(&b->dev, b->host, 0);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&b->done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    // a block that cannot be used stays out of the pool (never freed: no
+    // synchronising call on this path either)
+    delete b;
+    return hip_fail(e, "work-list block set-up");
+  }
+  b->bytes = cap;
+  *out = b;
   return BIA_OK;
+}
+
+void pin_release(bia::PinBlock* b) {
+  if (b == nullptr) return;
+  std::lock_guard<std::mutex> lock(g_pin_pool.mu);
+  g_pin_pool.returned.push_back(b);
+}
+
+bool gpu_visible() {
+  int n = 0;
+  return hipGetDeviceCount(&n) == hipSuccess && n > 0;
 }
 
 // Work-list upload as a kernel on the run's stream (no copy-engine handoff
@@ -1916,22 +2001,38 @@ bia_status check_run(const bia_plan* plan, bia_mode mode, bool mla, const void* 
   return BIA_OK;
 }
 
+// Copies the plan's work list from its pinned block into the head of the
+// workspace on `stream`, then records the block's event. A block last read
+// on another stream is waited for on this one first (no host wait), so the
+// event always covers every upload that has read the block.
 bia_status upload(const bia_plan* plan, void* workspace, hipStream_t stream) {
-  bia_status st = ensure_pinned(plan);
-  if (st != BIA_OK) return st;
   const size_t bytes = plan->d.blob_bytes;
   if (bytes == 0) return BIA_OK;
-  if (bytes % 16 != 0) {  // every list entry is 16 or 32 bytes
-    hipError_t e = hipMemcpyAsync(workspace, plan->pinned, bytes, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
-    return BIA_OK;
+  bia::PinBlock* b = plan->pin;
+  if (b == nullptr)
+    return bia::fail(BIA_ERR_HIP, "the plan holds no pinned work list (no GPU was visible "
+                                  "when it was made)");
+  hipError_t e = hipSuccess;
+  if (b->recorded && b->last_stream != stream) {
+    e = hipStreamWaitEvent(stream, b->done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(work list)");
   }
-  const int64_t n = static_cast<int64_t>(bytes / 16);
-  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
-  hipLaunchKernelGGL(upload_kernel, dim3(grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(plan->pinned_dev), static_cast<uint4*>(workspace), n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "work-list upload launch");
+  if (bytes % 16 != 0) {  // every list entry is 16 or 32 bytes
+    e = hipMemcpyAsync(workspace, b->host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  } else {
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    const unsigned grid =
+        static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
+    hipLaunchKernelGGL(upload_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const uint4*>(b->dev), static_cast<uint4*>(workspace), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "work-list upload launch");
+  }
+  e = hipEventRecord(b->done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(work list)");
+  b->recorded = true;
+  b->last_stream = stream;
   return BIA_OK;
 }
 
@@ -1987,10 +2088,35 @@ void launch_decode_g(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
 
 }  // namespace
 
+extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
+                                      const int32_t* kv_indptr, const int32_t* page_table,
+                                      int32_t batch, int32_t num_qo_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t split_size, uint32_t flags,
+                                      bia_plan** out_plan) {
+  bia_status st = bia::plan_create_host(mode, qo_indptr, kv_indptr, page_table, batch,
+                                        num_qo_heads, num_kv_heads, head_dim, page_size,
+                                        num_pages, split_size, flags, out_plan);
+  if (st != BIA_OK) return st;
+  bia_plan* plan = *out_plan;
+  // The pinned copy of the work list is made here, never in a run call. A
+  // process that sees no GPU gets a plan it can inspect but not run.
+  if (plan->d.blob_bytes == 0 || !gpu_visible()) return BIA_OK;
+  st = pin_acquire(plan->d.blob_bytes, &plan->pin);
+  if (st != BIA_OK) {
+    bia::plan_free_host(plan);
+    *out_plan = nullptr;
+    return st;
+  }
+  std::memcpy(plan->pin->host, plan->d.blob.data(), plan->d.blob_bytes);
+  return BIA_OK;
+}
+
 extern "C" void bia_plan_destroy(bia_plan* plan) {
   if (plan == nullptr) return;
-  if (plan->pinned != nullptr) (void)hipHostFree(plan->pinned);
-  delete plan;
+  pin_release(plan->pin);  // reused only after its last upload has run
+  bia::plan_free_host(plan);
 }
 
 extern "C" bia_status bia_prefill_paged(const bia_plan* plan, const void* q, const void* k_pool,

@@ -216,13 +216,11 @@ static bia_status check_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_
   return BIA_OK;
 }
 
-extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
-                                      const int32_t* kv_indptr,
-                                      const int32_t* page_table, int32_t batch,
-                                      int32_t num_qo_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t page_size,
-                                      int32_t num_pages, int32_t split_size,
-                                      uint32_t flags, bia_plan** out_plan) {
+bia_status bia::plan_create_host(bia_mode mode, const int32_t* qo_indptr,
+                                 const int32_t* kv_indptr, const int32_t* page_table,
+                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                 int32_t split_size, uint32_t flags, bia_plan** out_plan) {
   if (out_plan == nullptr) return fail(BIA_ERR_INVALID_ARG, "out_plan is NULL");
   *out_plan = nullptr;
   if (mode != BIA_MODE_PREFILL && mode != BIA_MODE_DECODE)
@@ -344,6 +342,8 @@ extern "C" bia_status bia_plan_create(bia_mode mode, const int32_t* qo_indptr,
   *out_plan = plan;
   return BIA_OK;
 }
+
+void bia::plan_free_host(bia_plan* plan) { delete plan; }
 
 extern "C" size_t bia_plan_workspace_bytes(const bia_plan* plan) {
   return plan == nullptr ? 0 : plan->d.ws_bytes;

@@ -77,6 +77,20 @@ struct PlanData {
 void set_error(const char* fmt, ...);
 bia_status fail(bia_status st, const char* fmt, ...);
 
+// The host half of bia_plan_create: validates the batch and builds the plan
+// (work list, merge list, append list, workspace layout). Plain C++; the C
+// entry point in the launch layer adds the pinned copy of the work list.
+bia_status plan_create_host(bia_mode mode, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* page_table, int32_t batch, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t split_size, uint32_t flags,
+                            bia_plan** out_plan);
+// Frees the host part of a plan (the launch layer returns its pinned block
+// first).
+void plan_free_host(bia_plan* plan);
+
+struct PinBlock;  // pinned work-list block of the launch layer's pool
+
 // Fixed-capacity decode planned on the device (graph-capturable). Request r
 // of a call has kv head h's partition s at item (r * Hkv + h) * max_splits + s
 // and its merge at r * Hkv + h; partition s of (r, h) keeps its partial states
@@ -95,8 +109,9 @@ struct DecodeGraphData {
 // The opaque handles of the C ABI.
 struct bia_plan {
   bia::PlanData d;
-  void* pinned = nullptr;      // pinned copy of d.blob, made by the launch layer
-  void* pinned_dev = nullptr;  // the same memory as the device addresses it
+  // Pinned copy of d.blob, drawn from the launch layer's pool when the plan
+  // is made (NULL when no GPU was visible then, or the blob is empty).
+  bia::PinBlock* pin = nullptr;
 };
 
 struct bia_decode_graph {
