@@ -175,6 +175,30 @@ bia_status bia_decode_paged(const bia_plan* plan, const void* q,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * bia_decode_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same output bits, with the workspace
+ * taken from a library-owned static device array of
+ * BIA_STATIC_WORKSPACE_BYTES on each GPU instead of a caller buffer. The
+ * caller still passes the plan, inputs and outputs (as for bia_decode_paged,
+ * on the current device's stream); the call allocates nothing (the plan's
+ * pinned work list was taken when the plan was made).
+ *   BIA_ERR_WORKSPACE: bia_plan_workspace_bytes(plan) exceeds
+ *   BIA_STATIC_WORKSPACE_BYTES (about 32 MiB holds a batch of 64 requests
+ *   with contexts of up to 32768 tokens at 8 kv heads x 4 q heads, D 128).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: each call writes its work
+ * list and partial states before reading them). Calls that can overlap on
+ * one GPU (on two streams, or from two threads) race on it and must not be
+ * made.
+ */
+#define BIA_STATIC_WORKSPACE_BYTES (32u << 20)
+bia_status bia_decode_paged_static(const bia_plan* plan, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* page_table_dev, float sm_scale,
+                                   void* out, float* lse, void* stream);
+
+/*
  * Latent (MLA) attention over a paged latent cache, absorbed form: the MLA
  * decode path that the pages name as lacking a deterministic mode (sglang PR
  * #43612, Summary), given the same fixed-split, fixed-order treatment as the

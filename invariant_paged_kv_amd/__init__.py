@@ -22,11 +22,12 @@ from ._lib import (BIA_DECODE_SPLIT, BIA_KV_TILE, BIA_MODE_DECODE,
                    BIA_MLA_MAX_SPLIT, BIA_MLA_QK_DIM, BIA_MLA_V_DIM, BIA_MODE_PREFILL,
                    BIA_PAGE_SIZE,
                    BIA_PLAN_MLA, BIA_PLAN_STRICT_CHUNK_ALIGN,
-                   BIA_PREFILL_SPLIT, BIA_Q_TILE_ROWS, BiaError, DecodeGraph, Plan,
+                   BIA_PREFILL_SPLIT, BIA_Q_TILE_ROWS, BIA_STATIC_WORKSPACE_BYTES,
+                   BiaError, DecodeGraph, Plan,
                    bia_append_paged_kv, bia_decode_graph_create,
                    bia_decode_graph_destroy, bia_decode_graph_read_flags,
                    bia_decode_graph_run, bia_decode_graph_workspace_bytes,
-                   bia_decode_paged,
+                   bia_decode_paged, bia_decode_paged_static,
                    bia_last_error, bia_merge_states, bia_mla_decode_paged,
                    bia_mla_prefill_paged, bia_plan_create,
                    bia_plan_destroy, bia_plan_workspace_bytes,
@@ -37,9 +38,9 @@ __all__ = [
     "BIA_DECODE_SPLIT", "BIA_KV_TILE", "BIA_MLA_MAX_SPLIT", "BIA_MLA_QK_DIM", "BIA_MLA_V_DIM",
     "BIA_MODE_DECODE",
     "BIA_MODE_PREFILL", "BIA_PAGE_SIZE", "BIA_PLAN_MLA", "BIA_PLAN_STRICT_CHUNK_ALIGN", "BIA_PREFILL_SPLIT", "BIA_Q_TILE_ROWS",
-    "BiaError", "DecodeGraph", "Plan", "bia_append_paged_kv", "bia_decode_graph_create",
+    "BIA_STATIC_WORKSPACE_BYTES", "BiaError", "DecodeGraph", "Plan", "bia_append_paged_kv", "bia_decode_graph_create",
     "bia_decode_graph_destroy", "bia_decode_graph_read_flags", "bia_decode_graph_run",
-    "bia_decode_graph_workspace_bytes", "bia_decode_paged", "bia_last_error",
+    "bia_decode_graph_workspace_bytes", "bia_decode_paged", "bia_decode_paged_static", "bia_last_error",
     "bia_merge_states", "bia_mla_decode_paged", "bia_mla_prefill_paged", "bia_plan_create",
     "bia_plan_destroy", "bia_plan_workspace_bytes", "bia_prefill_chunk_align",
     "bia_prefill_paged", "lib_path", "load_library",

@@ -73,6 +73,8 @@ def load_library():
     lib.bia_prefill_paged.argtypes = run_args
     lib.bia_decode_paged.restype = i32
     lib.bia_decode_paged.argtypes = run_args
+    lib.bia_decode_paged_static.restype = i32
+    lib.bia_decode_paged_static.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp]
     mla_args = [vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.bia_mla_prefill_paged.restype = i32
     lib.bia_mla_prefill_paged.argtypes = mla_args
@@ -284,6 +286,36 @@ def bia_decode_paged(plan: Plan, q, k_pool, v_pool, page_table_dev, sm_scale, ou
     """Paged decode, one query token per request (see ``bia_decode_paged``)."""
     _run(load_library().bia_decode_paged, plan, BIA_MODE_DECODE, q, k_pool, v_pool,
          page_table_dev, sm_scale, out, lse, workspace, stream)
+
+
+BIA_STATIC_WORKSPACE_BYTES = 32 << 20
+
+
+def bia_decode_paged_static(plan: Plan, q, k_pool, v_pool, page_table_dev, sm_scale, out,
+                            lse, stream=None):
+    """Paged decode with the library's static device workspace instead of a
+    caller buffer (see ``bia_decode_paged_static`` in bia.h): allocates
+    nothing; calls that can overlap on one GPU must not be made."""
+    torch = _torch()
+    if plan.mode != BIA_MODE_DECODE:
+        raise BiaError(1, "plan was made for the other mode")
+    if plan.mla:
+        raise BiaError(1, "an MLA plan runs through bia_mla_*_paged")
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    bf16 = torch.bfloat16
+    Hq, Hkv, D = plan.num_qo_heads, plan.num_kv_heads, plan.head_dim
+    qp = _dev_ptr(q, "q", bf16, (plan.total_q, Hq, D))
+    pool_shape = (plan.num_pages, BIA_PAGE_SIZE, Hkv, D)
+    kp = _dev_ptr(k_pool, "k_pool", bf16, pool_shape, device=dev)
+    vp = _dev_ptr(v_pool, "v_pool", bf16, pool_shape, device=dev)
+    ptp = _dev_ptr(page_table_dev, "page_table_dev", torch.int32,
+                   min_numel=plan.total_pages, device=dev)
+    op = _dev_ptr(out, "out", bf16, (plan.total_q, Hq, D), device=dev)
+    lp = None if lse is None else _dev_ptr(lse, "lse", torch.float32,
+                                          (plan.total_q, Hq), device=dev)
+    _check(load_library().bia_decode_paged_static(ctypes.c_void_p(plan.handle), qp, kp, vp,
+                                                  ptp, float(sm_scale), op, lp,
+                                                  _stream_handle(stream, q.device)))
 
 
 def _run_mla(fn, plan: Plan, mode, q, kv_pool, page_table_dev, sm_scale, out, lse,

@@ -2160,16 +2160,17 @@ extern "C" bia_status bia_prefill_paged(const bia_plan* plan, const void* q, con
   return BIA_OK;
 }
 
-extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* page_table_dev,
-                                       float sm_scale, void* out, float* lse, void* workspace,
-                                       size_t workspace_bytes, void* stream_handle) {
-  bia_status st = check_run(plan, BIA_MODE_DECODE, false, q, k_pool, v_pool, page_table_dev, sm_scale,
-                            out, workspace, workspace_bytes);
-  if (st != BIA_OK || plan->d.items.empty()) return st;
+namespace {
+
+// Decode of a planned batch with the workspace at `workspace` (the caller's
+// buffer, or the static one below).
+bia_status run_decode(const bia_plan* plan, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* page_table_dev, float sm_scale,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream_handle) {
   const bia::PlanData& d = plan->d;
   hipStream_t stream = static_cast<hipStream_t>(stream_handle);
-  st = upload(plan, workspace, stream);
+  bia_status st = upload(plan, workspace, stream);
   if (st != BIA_OK) return st;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const float scale_log2 = sm_scale * kLog2e;
@@ -2192,6 +2193,73 @@ extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return BIA_OK;
+}
+
+// Workspace of bia_decode_paged_static: a file-scope device array, one copy
+// per GPU, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up on the
+// entry point's first call on that device and kept per device.
+constexpr size_t kStaticWsBytes = BIA_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+bia_status static_workspace(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return bia::fail(BIA_ERR_UNSUPPORTED, "device %d outside the %d the static workspace "
+                                          "table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(static workspace)");
+    if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % bia::kWsAlign != 0)
+      return bia::fail(BIA_ERR_HIP, "static workspace address %p is not %zu-byte aligned",
+                       ptr, bia::kWsAlign);
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return BIA_OK;
+}
+
+}  // namespace
+
+extern "C" bia_status bia_decode_paged(const bia_plan* plan, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* page_table_dev,
+                                       float sm_scale, void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream_handle) {
+  bia_status st = check_run(plan, BIA_MODE_DECODE, false, q, k_pool, v_pool, page_table_dev, sm_scale,
+                            out, workspace, workspace_bytes);
+  if (st != BIA_OK || plan->d.items.empty()) return st;
+  return run_decode(plan, q, k_pool, v_pool, page_table_dev, sm_scale, out, lse, workspace,
+                    workspace_bytes, stream_handle);
+}
+
+extern "C" bia_status bia_decode_paged_static(const bia_plan* plan, const void* q,
+                                              const void* k_pool, const void* v_pool,
+                                              const int32_t* page_table_dev, float sm_scale,
+                                              void* out, float* lse, void* stream_handle) {
+  if (plan != nullptr && plan->d.ws_bytes > kStaticWsBytes)
+    return bia::fail(BIA_ERR_WORKSPACE,
+                     "plan needs %zu bytes of workspace, above the %zu-byte static workspace",
+                     plan->d.ws_bytes, kStaticWsBytes);
+  // the checks of bia_decode_paged, with a stand-in for the workspace (its
+  // address is looked up only once the call is known to run)
+  bia_status st = check_run(plan, BIA_MODE_DECODE, false, q, k_pool, v_pool, page_table_dev,
+                            sm_scale, out, reinterpret_cast<void*>(bia::kWsAlign),
+                            kStaticWsBytes);
+  if (st != BIA_OK || plan->d.items.empty()) return st;
+  void* ws = nullptr;
+  st = static_workspace(&ws);
+  if (st != BIA_OK) return st;
+  return run_decode(plan, q, k_pool, v_pool, page_table_dev, sm_scale, out, lse, ws,
+                    kStaticWsBytes, stream_handle);
 }
 
 namespace {
