@@ -135,3 +135,36 @@ def test_decode_run_to_run():
     o1, l1 = run_decode(b)
     o2, l2 = run_decode(b)
     assert bits_equal(o1, o2) and bits_equal(l1, l2)
+
+
+def _filler_requests(B, rng):
+    """B short requests with their own seeds: some fresh prefills, some chunks
+    over a cached prefix, some empty."""
+    qo = rng.integers(0, 300, size=B)
+    kv = qo + rng.integers(0, 600, size=B)
+    return [W.Request(int(a), int(b), 9000 + 97 * B + i) for i, (a, b) in enumerate(zip(qo, kv))]
+
+
+def test_prefill_probe_batch_sizes_1_to_64():
+    """A probe prefill request (a 600-token chunk over a 900-token cached
+    prefix, its own seed) at a varying position in batches of 1..64 seeded
+    neighbours, with page ids re-drawn per batch: its out/lse bits never
+    change, at the default split and at a split that merges partitions."""
+    probe = W.Request(600, 1500, 4242)
+    refs = {}
+    for B in range(1, 65):
+        pos = (B * 13 // 7) % B
+        rng = np.random.Generator(np.random.PCG64(500 + B))
+        reqs = _filler_requests(B, rng)
+        reqs[pos] = probe
+        b = W.make_batch(reqs, num_pages=8192, batch_seed=700 + B, device=DEV, **W.QWEN3_8B)
+        for split in (4096, 512):
+            say(f"prefill probe B={B} pos={pos} split={split}")
+            out, lse = run_prefill(b, split=split)
+            o, l = out[rows_of(b, pos)].clone(), lse[rows_of(b, pos)].clone()
+            if split not in refs:
+                refs[split] = (o, l)
+                assert_parity(out, lse, b, [pos], what=f"prefill probe vs oracle split {split}")
+            else:
+                assert bits_equal(refs[split][0], o) and bits_equal(refs[split][1], l), \
+                    f"prefill probe differs at B={B} split={split}"

@@ -430,3 +430,51 @@ def host_subset(b: PagedBatch, reqs):
             if reqs else np.zeros(0, dtype=np.int64))
     q = b.q[torch.as_tensor(rows, device=b.q.device)].cpu()
     return q, kp, vp, qo_ip, kv_ip, np.arange(len(pages)), rows
+
+
+def jump_batch(qo_lens, kv_lens, jump_at, *, num_qo_heads: int, num_kv_heads: int,
+               head_dim: int, seed: int, num_pages: int, c: float = 16.0,
+               device="cpu") -> PagedBatch:
+    """Keys whose logit leaps far above everything before it: per request and
+    kv head a direction u ~ N(0, 1); q = u (of the head's kv head) + N(0,
+    0.3^2); keys and values N(0, 1), except key ``jump_at[r]`` (if inside the
+    request) = c u. With c = 16 that key scores about c |u|^2 / sqrt(D), some
+    180 natural (260 base-2) units, far more than the 128 base-2 units past
+    which exp2 against the row's earlier maximum overflows fp32. One PCG64
+    stream per request."""
+    qs, ks, vs = [], [], []
+    g_size = num_qo_heads // num_kv_heads
+    for r, (qo, kv) in enumerate(zip(qo_lens, kv_lens)):
+        g = np.random.Generator(np.random.PCG64(seed * 1019 + r))
+        u = g.standard_normal((num_kv_heads, head_dim), dtype=np.float32)
+        k = g.standard_normal((kv, num_kv_heads, head_dim), dtype=np.float32)
+        v = g.standard_normal((kv, num_kv_heads, head_dim), dtype=np.float32)
+        j = int(jump_at[r])
+        if 0 <= j < kv:
+            k[j] = c * u
+        uq = np.repeat(u, g_size, axis=0)[None]
+        q = uq + 0.3 * g.standard_normal((qo, num_qo_heads, head_dim), dtype=np.float32)
+        qs.append(torch.from_numpy(q))
+        ks.append(torch.from_numpy(k))
+        vs.append(torch.from_numpy(v))
+    return assemble_batch(qo_lens, kv_lens, qs, ks, vs, num_pages=num_pages,
+                          batch_seed=seed, device=device)
+
+
+def identical_keys_batch(qo_lens, kv_lens, *, num_qo_heads: int, num_kv_heads: int,
+                         head_dim: int, seed: int, num_pages: int,
+                         device="cpu") -> PagedBatch:
+    """Every key of a request (per kv head) is the same vector w ~ N(0, 1);
+    q and v are N(0, 1). One PCG64 stream per request. Returned with the
+    contiguous copies (``k_seq``/``v_seq``)."""
+    qs, ks, vs = [], [], []
+    for r, (qo, kv) in enumerate(zip(qo_lens, kv_lens)):
+        g = np.random.Generator(np.random.PCG64(seed * 1021 + r))
+        w = g.standard_normal((1, num_kv_heads, head_dim), dtype=np.float32)
+        ks.append(torch.from_numpy(np.repeat(w, kv, axis=0)))
+        vs.append(torch.from_numpy(g.standard_normal((kv, num_kv_heads, head_dim),
+                                                     dtype=np.float32)))
+        qs.append(torch.from_numpy(g.standard_normal((qo, num_qo_heads, head_dim),
+                                                     dtype=np.float32)))
+    return assemble_batch(qo_lens, kv_lens, qs, ks, vs, num_pages=num_pages,
+                          batch_seed=seed, device=device, keep_seq=True)
