@@ -39,7 +39,7 @@ def test_python_binding_has_every_entry_point():
                  "bia_decode_graph_create", "bia_decode_graph_destroy",
                  "bia_decode_graph_workspace_bytes", "bia_decode_graph_run",
                  "bia_decode_graph_read_flags", "bia_mla_prefill_paged",
-                 "bia_mla_decode_paged"]:
+                 "bia_mla_decode_paged", "bia_decode_paged_static"]:
         assert name in declared_functions()
         assert callable(getattr(bia, name)), name
 
