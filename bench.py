@@ -12,7 +12,10 @@ call's time from HIP events on its stream); ``decode.value`` is decode KV
 GB/s (bytes of K and V read once per kv head, plus q, out, lse and page ids).
 ``roofline`` is the prefill kernel against the bf16 MFMA peak,
 ``decode.roofline`` the decode kernel against HBM bandwidth. ``cpu_baseline``
-is the float64 CPU oracle timed on a bounded sample of the same inputs.
+is the float64 CPU oracle timed on the same inputs (the whole prefill and the
+whole decode batch), with the host's CPU model and core counts. ``mixed`` is
+the long-context workload: a 65536-token prefill in four 16384-token chunks,
+each step beside 128 lognormal-context decodes.
 """
 from __future__ import annotations
 
@@ -98,13 +101,30 @@ class Timer:
 
 
 def _oracle_threads() -> int:
+    """Threads of the BLAS pool the float64 oracle's matrix products run on."""
     from threadpoolctl import threadpool_info
     return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
 
 
-def cpu_baseline_prefill(b, n=2):
+def host_info() -> dict:
+    """The host the oracle is timed on: CPU model, CPUs this process may run
+    on, BLAS threads the oracle uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus_available": len(os.sched_getaffinity(0)),
+            "blas_threads": _oracle_threads()}
+
+
+def cpu_baseline_prefill(b, n=8):
     """The float64 CPU oracle on the first ``n`` requests of the prefill batch
-    (4096 tokens each, all 32 q heads): n/8 of the prefill workload, same
+    (4096 tokens each, all 32 q heads; n = 8 is the whole workload), same
     inputs."""
     import oracle
     import workloads as W
@@ -113,14 +133,16 @@ def cpu_baseline_prefill(b, n=2):
     oracle.attention_paged(q, kp, vp, qo_ip, kv_ip, pt, b.num_kv_heads, b.sm_scale)
     dt = time.perf_counter() - t
     fl = prefill_flops(np.diff(qo_ip), np.diff(kv_ip), b.num_qo_heads, b.head_dim)
+    what = "the whole prefill workload" if n == b.batch else f"{n}/{b.batch} of the prefill workload"
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": _oracle_threads(), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"prefill requests 0..{n - 1} of 8 (4096 tokens each, all 32 q "
-                      f"heads): {n}/8 of the prefill workload, same seeded inputs"}
+            "sample": f"prefill requests 0..{n - 1} of {b.batch} (4096 tokens each, all 32 q "
+                      f"heads): {what}, same seeded inputs", **host_info()}
 
 
-def cpu_baseline_decode(b, n=16):
-    """The float64 CPU oracle on the first ``n`` decode requests."""
+def cpu_baseline_decode(b, n=64):
+    """The float64 CPU oracle on the first ``n`` decode requests (n = 64 is
+    the whole batch)."""
     import oracle
     import workloads as W
     reqs = list(range(n))
@@ -131,8 +153,89 @@ def cpu_baseline_decode(b, n=16):
     by = decode_bytes(np.diff(kv_ip), b.num_qo_heads, b.num_kv_heads, b.head_dim)
     return {"value": round(by / dt / 1e9, 4), "unit": "GB/s",
             "cores": _oracle_threads(), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"decode requests 0..{n - 1} of 64 "
-                      f"({int(np.diff(kv_ip).sum())} context tokens), same seeded inputs"}
+            "sample": f"decode requests 0..{n - 1} of {b.batch} "
+                      f"({int(np.diff(kv_ip).sum())} context tokens), same seeded inputs",
+            **host_info()}
+
+
+def mixed_steps(torch, bia, W, stream, dev, rounds=3):
+    """The mixed long-context workload: one 65536-token request prefilled in
+    four 16384-token chunks (chunk c: qo 16384, kv 16384 (c + 1), over its
+    cached prefix pages, split 4096) plus 128 decodes with lognormal contexts
+    (median 4096, sigma 1, cap 131072; split 2048). One step = prefill chunk c
+    + the 128 decodes. Per step: prefill TFLOP/s and decode GB/s from HIP
+    events on the stream, with their roofline fractions; averaged over
+    ``rounds`` passes of the four steps after one untimed pass."""
+    seq = W.make_sequence(65536, seed=5, num_pages=8192, device=dev)
+    ctx = W.mixed_decode_lengths()
+    db = W.decode_batch(128, ctx_lens=ctx, seed=5, num_pages=131072, device=dev,
+                        max_ctx=131072)
+    heads = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128)
+    chunks = [seq.chunk(lo, hi) for lo, hi in W.chunk_bounds(65536, 16384)]
+    s_pt = torch.as_tensor(seq.batch.page_table, dtype=torch.int32, device=dev)
+    d_pt = torch.as_tensor(db.page_table, dtype=torch.int32, device=dev)
+    p_out = torch.empty(16384, 32, 128, dtype=torch.bfloat16, device=dev)
+    p_lse = torch.empty(16384, 32, dtype=torch.float32, device=dev)
+    d_out = torch.empty_like(db.q)
+    d_lse = torch.empty(db.q.shape[:2], dtype=torch.float32, device=dev)
+
+    def plans(ch):
+        pp = bia.bia_plan_create(bia.BIA_MODE_PREFILL, ch.qo_indptr, ch.kv_indptr,
+                                 ch.page_table, num_pages=ch.num_pages,
+                                 split_size=bia.BIA_PREFILL_SPLIT, **heads)
+        dp = bia.bia_plan_create(bia.BIA_MODE_DECODE, db.qo_indptr, db.kv_indptr,
+                                 db.page_table, num_pages=db.num_pages,
+                                 split_size=bia.BIA_DECODE_SPLIT, **heads)
+        return pp, dp
+
+    p_bytes, d_bytes_ws = 256, 256
+    for ch in chunks:
+        pp, dp = plans(ch)
+        p_bytes = max(p_bytes, pp.workspace_bytes)
+        d_bytes_ws = max(d_bytes_ws, dp.workspace_bytes)
+        pp.close(), dp.close()
+    p_ws = torch.empty(p_bytes, dtype=torch.uint8, device=dev)
+    d_ws = torch.empty(d_bytes_ws, dtype=torch.uint8, device=dev)
+    timers = [(Timer(torch, stream), Timer(torch, stream)) for _ in chunks]
+    for r in range(rounds + 1):
+        for c, ch in enumerate(chunks):
+            pp, dp = plans(ch)
+            pt_t, dt_t = timers[c]
+            s = pt_t.start() if r else None
+            bia.bia_prefill_paged(pp, ch.q, ch.k_pool, ch.v_pool, s_pt, ch.sm_scale, p_out,
+                                  p_lse, p_ws, stream)
+            if r:
+                pt_t.stop(s)
+                s = dt_t.start()
+            bia.bia_decode_paged(dp, db.q, db.k_pool, db.v_pool, d_pt, db.sm_scale, d_out,
+                                 d_lse, d_ws, stream)
+            if r:
+                dt_t.stop(s)
+            pp.close(), dp.close()
+    torch.cuda.synchronize()
+    d_bytes = decode_bytes(db.kv_lens(), 32, 8, 128)
+    steps = []
+    for c, ch in enumerate(chunks):
+        p_ms, d_ms = timers[c][0].mean_ms(), timers[c][1].mean_ms()
+        fl = prefill_flops(ch.qo_lens(), ch.kv_lens(), 32, 128)
+        tf = fl / (p_ms * 1e-3) / 1e12
+        gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        steps.append({"chunk": [16384 * c, 16384 * (c + 1)], "prefill_ms": round(p_ms, 4),
+                      "prefill_TFLOP/s": round(tf, 1),
+                      "prefill_frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "decode_ms": round(d_ms, 4), "decode_GB/s": round(gbs, 1),
+                      "decode_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "step_ms": round(p_ms + d_ms, 4)})
+    tot_fl = sum(prefill_flops(ch.qo_lens(), ch.kv_lens(), 32, 128) for ch in chunks)
+    tot_p = sum(x["prefill_ms"] for x in steps)
+    tot_d = sum(x["decode_ms"] for x in steps)
+    del seq, db, chunks, p_ws, d_ws
+    return {"workload": "65536-token prefill in 4 chunks of 16384 + 128 decodes, lognormal "
+                        "contexts (median 4096, sigma 1, cap 131072)",
+            "decode_kv_tokens": int(ctx.sum()), "steps": steps,
+            "prefill_TFLOP/s": round(tot_fl / (tot_p * 1e-3) / 1e12, 1),
+            "decode_GB/s": round(4 * d_bytes / (tot_d * 1e-3) / 1e9, 1),
+            "ms_per_step": round((tot_p + tot_d) / 4, 4)}
 
 
 def copy_bandwidth(torch, stream, dev, gib=2, reps=10):
@@ -412,6 +515,7 @@ def main():
         extras["sweep"] = decode_sweep(torch, bia, W, db, d_pt, stream, dev)
         extras["graph"] = decode_graph_replay(torch, bia, db, d_pt, stream, dev, d_out, d_lse)
         extras["mla"] = mla_extra(torch, bia, W, stream, dev)
+        extras["mixed"] = mixed_steps(torch, bia, W, stream, dev)
 
     p_flops = prefill_flops(pb.qo_lens(), pb.kv_lens(), 32, 128)
     d_bytes = decode_bytes(db.kv_lens(), 32, 8, 128)
@@ -471,6 +575,7 @@ def main():
         result["decode"]["sweep"] = extras["sweep"]
         result["decode"]["graph_replay"] = extras["graph"]
         result["mla"] = extras["mla"]
+        result["mixed"] = extras["mixed"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(pb)
         result["decode"]["cpu_baseline"] = cpu_baseline_decode(db)
