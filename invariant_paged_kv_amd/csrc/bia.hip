@@ -1691,15 +1691,12 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 // ((r * Hkv + h) * max_splits + s) * g + head-in-group; the request's merge is
 // at r * Hkv + h.
 //
-// Launch order (what the host planner's longest-first sort gives, computed
-// from kv_indptr alone by every workgroup): first the whole partitions of all
-// requests, partition-major, then the requests' partial last partitions,
-// longest first (ties by request index), then the empty slots (n_tok = 0: the decode kernel returns at once). Item index =
-// unit * Hkv + h, so consecutive workgroups, which the dispatcher deals
-// round-robin over the XCDs, are different kv heads of one (request,
-// partition); with (request, head, partition) order the XCD would follow the
-// partition index, and the XCDs holding the low partitions every request has
-// would get most of the work.
+// Launch order: the host planner's, computed from kv_indptr alone by every
+// workgroup. First the whole partitions of all requests in (request, kv
+// head, partition) order, packed (request r's start after the whole
+// partitions of the requests before it), then the requests' partial last
+// partitions, longest first (ties by request index, then kv head), then the
+// empty slots (n_tok = 0: the decode kernel returns at once).
 //
 // flags[r] is 0 for a valid request, else a reason bit. An invalid request
 // reads no keys: the first of its slots gets an item with kv_len = 0 (its rows
@@ -1710,7 +1707,6 @@ append_kernel(const bia::AppendItem* __restrict__ items, const uint16_t* __restr
 constexpr int32_t kGraphBadKvLen = 1;  // kv_len < 1 or > max_kv_len
 constexpr int32_t kGraphBadTable = 2;  // pages past page_table_capacity
 constexpr int32_t kGraphBadPage = 4;   // a page id outside [0, num_pages)
-constexpr int kGraphStagedBatch = 8192;  // requests whose partition counts the planner keeps in LDS
 
 __global__ void __launch_bounds__(kThreads)
 decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
@@ -1718,9 +1714,8 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
                          int split, int max_splits, int max_kv_len, int num_pages,
                          int page_table_capacity, int32_t* __restrict__ flags,
                          WorkItem* __restrict__ items, MergeItem* __restrict__ merges) {
-  __shared__ int64_t sm_red[4][kThreads];
+  __shared__ int64_t sm_red[5][kThreads];
   __shared__ int32_t sm_bad;
-  __shared__ int32_t sm_nf[kGraphStagedBatch];
   const int r = blockIdx.x;
   const int batch = gridDim.x;
   const int tid = threadIdx.x;
@@ -1748,17 +1743,20 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   };
   const int64_t my_tiles = partial_tiles(r);
   // integer sums over the requests (exact in any order): pages before r, whole
-  // partitions of all, partial partitions of all and of those launched before
-  // r's (more tiles, or as many and an earlier request)
-  int64_t pages_before = 0, all_nf = 0, all_np = 0, np_before = 0;
+  // partitions of all and of the requests before r, partial partitions of all
+  // and of those launched before r's (more tiles, or as many and an earlier
+  // request)
+  int64_t pages_before = 0, all_nf = 0, all_np = 0, np_before = 0, nf_before = 0;
   for (int q = tid; q < batch; q += kThreads) {
     const int64_t len = static_cast<int64_t>(kv_indptr[q + 1]) - kv_indptr[q];
     int32_t nf, np;
     reserve(q, nf, np);
-    if (batch <= kGraphStagedBatch) sm_nf[q] = nf;  // read batch times per partition below
     all_nf += nf;
     all_np += np;
-    if (q < r) pages_before += len > 0 ? (len + 15) / 16 : 0;
+    if (q < r) {
+      pages_before += len > 0 ? (len + 15) / 16 : 0;
+      nf_before += nf;
+    }
     if (np != 0) {
       const int64_t tq = partial_tiles(q);
       if (tq > my_tiles || (tq == my_tiles && q < r)) np_before += 1;
@@ -1768,12 +1766,13 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   sm_red[1][tid] = all_nf;
   sm_red[2][tid] = all_np;
   sm_red[3][tid] = np_before;
+  sm_red[4][tid] = nf_before;
   if (tid == 0) sm_bad = 0;
   __syncthreads();
   for (int w = kThreads / 2; w > 0; w >>= 1) {
     if (tid < w) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) sm_red[k][tid] += sm_red[k][tid + w];
+      for (int k = 0; k < 5; ++k) sm_red[k][tid] += sm_red[k][tid + w];
     }
     __syncthreads();
   }
@@ -1781,6 +1780,7 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   const int64_t n_full = sm_red[1][0];        // whole-partition units of the launch
   const int64_t n_used = n_full + sm_red[2][0];
   const int64_t my_partial_unit = n_full + sm_red[3][0];
+  const int64_t my_full_unit0 = sm_red[4][0];  // r's whole partitions start here
 
   const int64_t kv_len = static_cast<int64_t>(kv_indptr[r + 1]) - kv_indptr[r];
   int32_t bad = 0;
@@ -1806,24 +1806,13 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
   const int32_t n_res = nf_r + np_r;          // this request's partitions (= its slots)
   const int32_t n_splits = bad ? 0 : n_res;
   for (int sp = tid; sp < n_res; sp += kThreads) {
-    int64_t unit;
-    if (sp < nf_r) {  // whole partition sp: after every whole partition with index < sp,
-                      // and after partition sp of the requests before r
-      unit = 0;
-      for (int q = 0; q < batch; ++q) {
-        int32_t nf, np;
-        if (batch <= kGraphStagedBatch) {
-          nf = sm_nf[q];
-        } else {
-          reserve(q, nf, np);
-        }
-        unit += min(nf, sp) + (q < r && nf > sp ? 1 : 0);
-      }
-    } else {
-      unit = my_partial_unit;
-    }
 #pragma unroll 1
     for (int h = 0; h < num_kv_heads; ++h) {
+      // whole partition sp of kv head h: (request, kv head, partition) order;
+      // the partial one: its rank among the partial partitions
+      const int64_t idx = sp < nf_r ? (my_full_unit0 * num_kv_heads +
+                                       static_cast<int64_t>(h) * nf_r + sp)
+                                    : my_partial_unit * num_kv_heads + h;
       WorkItem w{r, 0, 0, 0, 0, h, 0, -1};
       if (bad) {
         w.n_tok = sp == 0 ? 1 : 0;  // kv_len 0: the empty state
@@ -1836,7 +1825,7 @@ decode_graph_plan_kernel(const int32_t* __restrict__ kv_indptr,
         w.kv_begin = sp * split;
         w.state = n_splits > 1 ? static_cast<int32_t>(slot * group) : -1;
       }
-      items[unit * num_kv_heads + h] = w;
+      items[idx] = w;
     }
   }
   // this workgroup's share of the empty slots after the used ones

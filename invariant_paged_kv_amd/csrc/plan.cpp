@@ -178,10 +178,15 @@ static bia_status build(PlanData& d, const int32_t* qo_indptr,
     return BIA_OK;
   }
   // Decode items share no pages: longest first, so the tail of the launch is
-  // short work; a stable sort keeps the plan itself deterministic.
+  // short work. Whole partitions first, in (request, kv head, partition)
+  // order, then the partial last partitions by 64-key tiles (a stable sort:
+  // ties keep request, kv head order). The device planner of the
+  // graph-capturable decode launches the same order.
   const int32_t split = d.split;
+  auto whole = [split](const WorkItem& w) { return w.kv_len - w.kv_begin >= split; };
   std::stable_sort(d.items.begin(), d.items.end(),
-                   [split](const WorkItem& a, const WorkItem& b) {
+                   [split, whole](const WorkItem& a, const WorkItem& b) {
+                     if (whole(a) != whole(b)) return whole(a);
                      return item_tiles(a, split) > item_tiles(b, split);
                    });
   return BIA_OK;

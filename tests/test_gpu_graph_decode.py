@@ -141,9 +141,10 @@ def test_invalid_requests_are_flagged():
 
 
 def test_device_plan_matches_host_plan():
-    """The device planner's work list holds the host planner's items (all
-    fields but the partial-state slot), each once, whole partitions first,
-    partial last partitions next, empty slots last."""
+    """The device planner's work list is the host planner's (all fields but
+    the partial-state slot) in the host's launch order: whole partitions in
+    (request, kv head, partition) order, partial last partitions longest
+    first, then the empty slots."""
     ctx = [4096, 1, 2048, 2049, 6000, 16384, 100, 12345, 4095]
     b = W.decode_batch(len(ctx), seed=91, num_pages=4096, device=DEV, ctx_lens=ctx)
     max_batch, max_kv, cap = 12, 16384, 4096
@@ -170,6 +171,8 @@ def test_device_plan_matches_host_plan():
     assert len(live) == len(host_items)
     key = lambda a: sorted(map(tuple, a[:, :7].tolist()))
     assert key(live) == key(host_items)
+    # the same launch order as the host plan
+    assert (dev_items[:len(live), :7] == np.asarray(host_items)[:, :7]).all()
     # order: whole partitions, then partial ones, then the empty slots
     n_live = len(live)
     assert (dev_items[n_live:, 1] == 0).all()
