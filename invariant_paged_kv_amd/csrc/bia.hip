@@ -761,8 +761,8 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 // (each holds D/8 of its dims, so 16-byte loads read whole rows) and a lane
 // group takes keys c*16 + ks and c*16 + 8 + ks (one page). Chunks rotate
 // through kDecodeBuffers (3) register buffers: the loads of a wave's next two
-// chunks are in flight while the current one is computed, and page ids are
-// read a chunk earlier still.
+// chunks are in flight while the current one is computed, and page ids
+// (scalar loads: a chunk is one page) are read a chunk earlier still.
 //
 // Scores: v_dot2_f32_bf16 partial dots, reduced over the 8 lanes with three
 // DPP adds. PV: the two keys' probabilities (bf16) and the two keys' values
@@ -848,7 +848,7 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   if (it.n_tok == 0) return;  // a fixed-capacity slot past the request's partitions
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int ks = lane >> 3;    // key slot of this lane's group
   const int part = lane & 7;   // which D/8 dims of the key this lane holds
 
@@ -881,34 +881,46 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   }
 
   const int n_chunks = (kv_end - it.kv_begin + CHUNK - 1) / CHUNK;
-  // page id of this lane group's keys in chunk c (both keys share a page)
+  // Page id of chunk c: a chunk is 16 keys from a multiple of 16 (partitions
+  // start at multiples of the split), so one page, the same for the whole
+  // wave: a scalar load, which waits on its own counter instead of behind
+  // the data loads in flight (any in-range page past the last chunk).
   auto page_of = [&](int c) -> int32_t {
-    const int key = it.kv_begin + CHUNK * c + ks;
-    return (c < n_chunks && key < kv_end) ? pt[key >> 4] : 0;
+    return pt[min(it.kv_begin + CHUNK * c, kv_end - 1) >> 4];
   };
+  // The 16-byte loads of chunk c (a key past the partition reads the
+  // partition's last key instead; such keys are zeroed before use, by
+  // zero_tail).
   auto load = [&](uint32_t (&kw)[2][W], uint32_t (&vw)[2][W], int c, int64_t page) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = it.kv_begin + CHUNK * c + 8 * i + ks;
-      if (key < kv_end) {
-        const int64_t off = (page * 16 + (key & 15)) * slot_stride + head_off;
+      const int key = min(it.kv_begin + CHUNK * c + 8 * i + ks, kv_end - 1);
+      const int64_t off = (page * 16 + (key & 15)) * slot_stride + head_off;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint4 a = *reinterpret_cast<const uint4*>(kp + off + 8 * u);
-          const uint4 b = *reinterpret_cast<const uint4*>(vp + off + 8 * u);
-          kw[i][4 * u] = a.x; kw[i][4 * u + 1] = a.y; kw[i][4 * u + 2] = a.z; kw[i][4 * u + 3] = a.w;
-          vw[i][4 * u] = b.x; vw[i][4 * u + 1] = b.y; vw[i][4 * u + 2] = b.z; vw[i][4 * u + 3] = b.w;
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < W; ++u) {
-          kw[i][u] = 0;
-          vw[i][u] = 0;
-        }
+      for (int u = 0; u < U; ++u) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kp + off + 8 * u);
+        const uint4 b = *reinterpret_cast<const uint4*>(vp + off + 8 * u);
+        kw[i][4 * u] = a.x; kw[i][4 * u + 1] = a.y; kw[i][4 * u + 2] = a.z; kw[i][4 * u + 3] = a.w;
+        vw[i][4 * u] = b.x; vw[i][4 * u + 1] = b.y; vw[i][4 * u + 2] = b.z; vw[i][4 * u + 3] = b.w;
       }
     }
   };
-  auto compute = [&](const uint32_t (&kw)[2][W], const uint32_t (&vw)[2][W], int c) {
+  // Keys of chunk c past the partition hold zeros (only the last chunk can
+  // reach past it: a uniform test).
+  auto zero_tail = [&](uint32_t (&kw)[2][W], uint32_t (&vw)[2][W], int c) {
+    if (it.kv_begin + CHUNK * (c + 1) <= kv_end) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool live = it.kv_begin + CHUNK * c + 8 * i + ks < kv_end;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        kw[i][u] = live ? kw[i][u] : 0u;
+        vw[i][u] = live ? vw[i][u] : 0u;
+      }
+    }
+  };
+  auto compute = [&](uint32_t (&kw)[2][W], uint32_t (&vw)[2][W], int c) {
+    zero_tail(kw, vw, c);
     float s[2][G];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -972,10 +984,14 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
   // use them. The order of the arithmetic does not depend on NB.
   constexpr int NB = kDecodeBuffers<G>;
   uint32_t kbuf[NB][2][W], vbuf[NB][2][W];
+  // Every step issues its chunk's loads, also for a chunk past the partition
+  // (those read its last key, in range and never used): with the same loads
+  // on every path the compiler's waits for chunk c leave the loads of the
+  // chunks after it in flight.
 #pragma unroll
   for (int k = 0; k + 1 < NB; ++k) {
     const int cl = wave + 4 * k;
-    if (cl < n_chunks) load(kbuf[k], vbuf[k], cl, page_of(cl));
+    load(kbuf[k], vbuf[k], cl, page_of(cl));
   }
   int32_t page_next = page_of(wave + 4 * (NB - 1));
   for (int c = wave; c < n_chunks; c += 4 * NB) {
@@ -984,7 +1000,7 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
       const int cc = c + 4 * k;
       if (cc >= n_chunks) break;  // uniform over the wave
       const int cl = cc + 4 * (NB - 1);
-      if (cl < n_chunks) load(kbuf[(k + NB - 1) % NB], vbuf[(k + NB - 1) % NB], cl, page_next);
+      load(kbuf[(k + NB - 1) % NB], vbuf[(k + NB - 1) % NB], cl, page_next);
       page_next = page_of(cl + 4);
       compute(kbuf[k], vbuf[k], cc);
     }
