@@ -1,13 +1,17 @@
 """KV append on the GPU: writing each request's new tokens into its pages
-reproduces the generator's pool bit for bit and touches nothing else, and a
-prefill over the appended pool equals the prefill over the original pool."""
+reproduces the generator's pool bit for bit and touches nothing else; read
+back through the oracle's own page/slot gather, every request's keys and
+values equal the generator's never-paged rows; and a prefill over the
+appended pool equals the prefill over the original pool and meets oracle
+parity."""
 import numpy as np
 import pytest
 import torch
 
 import invariant_paged_kv_amd as bia
+import oracle
 import workloads as W
-from gpu_util import bits_equal, page_table_dev, run_prefill, say
+from gpu_util import assert_parity, bits_equal, page_table_dev, run_prefill, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -35,13 +39,15 @@ def test_append_then_attend(mode):
                 W.Request(1, 1000, 704), W.Request(40, 41, 705)]
     else:
         reqs = [W.Request(1, int(c), 710 + i) for i, c in enumerate([1, 17, 2048, 5000])]
-    b = W.make_batch(reqs, num_pages=1024, batch_seed=31, device=DEV, **W.QWEN3_8B)
+    b = W.make_batch(reqs, num_pages=1024, batch_seed=31, device=DEV, keep_seq=True,
+                     **W.QWEN3_8B)
     slots = torch.as_tensor(new_token_slots(b), device=DEV)
     Hkv, D = b.num_kv_heads, b.head_dim
-    kf = b.k_pool.view(-1, Hkv, D)
-    vf = b.v_pool.view(-1, Hkv, D)
-    k_new = kf[slots].contiguous()
-    v_new = vf[slots].contiguous()
+    # the new tokens' rows, from the generator's never-paged copies
+    k_new = torch.cat([b.k_seq[r][int(b.kv_lens()[r] - b.qo_lens()[r]):]
+                       for r in range(b.batch)]).to(DEV).contiguous()
+    v_new = torch.cat([b.v_seq[r][int(b.kv_lens()[r] - b.qo_lens()[r]):]
+                       for r in range(b.batch)]).to(DEV).contiguous()
     k_pool = b.k_pool.clone()
     v_pool = b.v_pool.clone()
     k_pool.view(-1, Hkv, D)[slots] = float("nan")      # the new tokens' slots are stale
@@ -56,6 +62,17 @@ def test_append_then_attend(mode):
     plan.close()
     # bitwise: NaN payloads in untouched slots compare equal as bits
     assert bits_equal(k_pool, b.k_pool) and bits_equal(v_pool, b.v_pool)
+    # the oracle's gather (its page/slot mapping) over the appended pool gives
+    # back every request's rows, old and new, exactly
+    offs = oracle.page_offsets(b.kv_lens(), b.page_size)
+    kp_h, vp_h = k_pool.cpu(), v_pool.cpu()
+    for r in range(b.batch):
+        kv = int(b.kv_lens()[r])
+        for h in range(Hkv):
+            kg = oracle.gather_request_kv(kp_h, b.page_table, int(offs[r]), kv, h)
+            vg = oracle.gather_request_kv(vp_h, b.page_table, int(offs[r]), kv, h)
+            assert np.array_equal(kg, b.k_seq[r][:, h, :].double().numpy())
+            assert np.array_equal(vg, b.v_seq[r][:, h, :].double().numpy())
     if mode == "prefill":
         o1, l1 = run_prefill(b)
         b2 = W.PagedBatch(b.qo_indptr, b.kv_indptr, b.page_table, b.num_pages, b.page_size,
@@ -63,3 +80,4 @@ def test_append_then_attend(mode):
                           k_pool, v_pool)
         o2, l2 = run_prefill(b2)
         assert bits_equal(o1, o2) and bits_equal(l1, l2)
+        assert_parity(o2, l2, b2, what="prefill over the appended pool")

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import assert_parity, bits_equal, run_prefill, say
+from gpu_util import assert_parity, bits_equal, run_prefill, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -23,6 +23,19 @@ def seq():
     s = W.make_sequence(6000, seed=17, num_pages=1024, device=DEV)
     out, lse = run_prefill(s.batch)
     return s, out, lse
+
+
+def test_unchunked_reference_parity(seq):
+    """The unchunked 6000-token rows every case below is compared with meet
+    oracle parity on the first and last 128 rows, every 61st row, and the
+    rows around each chunk and prefix boundary the cases use."""
+    s, of, lf = seq
+    say("6000-token unchunked reference vs oracle (sampled rows)")
+    rows = set(sample_rows(6000).tolist())
+    for c in (1, 511, 2048, 2560, 3200, 4097, 5888, 5997):
+        rows |= {max(0, c - 1), c, min(5999, c + 1)}
+    assert_parity(of, lf, s.batch, [0], {0: np.array(sorted(rows))},
+                  what="6000-token unchunked")
 
 
 def test_tiny_last_chunk(seq):
