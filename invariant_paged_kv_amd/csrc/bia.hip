@@ -1397,9 +1397,9 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
 
 // ---------------------------------------------------------------------------
 // Latent (MLA) decode with at most 16 q heads: one wave per work item (the
-// item's q heads are rows 0 .. Hq - 1 of the wave's 16), four consecutive
-// items per workgroup (measured faster than spreading the items over at
-// least one workgroup per CU), no workgroup barrier. Each wave streams its partition in
+// item's q heads are rows 0 .. Hq - 1 of the wave's 16), kMlaDecWaves (3)
+// consecutive items per workgroup (measured faster than spreading the items
+// over at least one workgroup per CU), no workgroup barrier. Each wave streams its partition in
 // 16-key tiles (one page each) through two LDS buffers of its own (DMA,
 // counted waits, the same swizzled unpadded rows as mla_kernel):
 //   S^T = K Q^T: 18 v_mfma_f32_16x16x32_bf16 (keys as M, rows as N);
@@ -1421,17 +1421,23 @@ __device__ __forceinline__ void mla_dec_wait(bool next_in_flight) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ void __launch_bounds__(kThreads, 1)
+// Items (one wave each) per workgroup; one workgroup per CU (LDS). Three
+// spread the B = 64, 16-head decode's items over more CUs than four in one
+// round (0.278-0.282 against 0.284-0.286 ms on one box); two need a second
+// round (0.331 ms).
+constexpr int kMlaDecWaves = 3;
+
+__global__ void __launch_bounds__(64 * kMlaDecWaves, 1)
 mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
                   const uint16_t* __restrict__ q, const uint16_t* __restrict__ kvp,
                   const int32_t* __restrict__ page_table, float scale_log2, int num_qo_heads,
                   int hb, int split, uint16_t* __restrict__ out, float* __restrict__ lse_out,
                   float* __restrict__ o_part, float* __restrict__ lse_part) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4][2][kMlaPageBytes];
-  __shared__ int32_t lds_pages[4][kMlaDecMaxPages];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMlaDecWaves][2][kMlaPageBytes];
+  __shared__ int32_t lds_pages[kMlaDecWaves][kMlaDecMaxPages];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int item = blockIdx.x * 4 + wave;
+  const int item = blockIdx.x * kMlaDecWaves + wave;
   if (item >= n_items) return;  // no barrier below: waves are independent
   const WorkItem it = items[item];
   if (it.n_tok == 0) return;
@@ -2285,7 +2291,8 @@ bia_status run_mla(const bia_plan* plan, bia_mode mode, const void* q, const voi
   int hb_shift = 0;
   while ((1 << hb_shift) < d.group) ++hb_shift;
   if (mode == BIA_MODE_DECODE && d.group <= 16 && d.split <= 16 * kMlaDecMaxPages) {
-    hipLaunchKernelGGL(mla_decode_kernel, dim3((L.n + 3) / 4), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(mla_decode_kernel, dim3((L.n + kMlaDecWaves - 1) / kMlaDecWaves),
+                       dim3(64 * kMlaDecWaves), 0, stream,
                        reinterpret_cast<const WorkItem*>(L.items), static_cast<int>(L.n),
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_pool),
                        page_table_dev, sm_scale * kLog2e, d.num_qo_heads, d.group, d.split, o,
