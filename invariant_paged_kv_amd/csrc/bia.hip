@@ -542,6 +542,21 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
       }
     }
 
+    // The item's first tile: every row with a visible key has no max yet, so
+    // below it would ask for the tile max and recompute its probabilities
+    // (lsum and O, still zero, scaled by zero). The max is taken here instead,
+    // as that path takes it, and the probabilities are computed once: the
+    // same values, sums and order, so the same bits.
+    if (j == 0) {
+      float xm = cur[0][0];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xm = fmaxf(xm, cur[kbk][v]);
+      const float mt = max_halves(xm) * scale_log2;
+      if (row_live && mt > m + kLazyMax) m = mt;  // m is -inf here
+    }
+
     // ---- phase A ----
     // Probabilities against the running max as it stands, p = exp2(s c - m),
     // one key pair per score MFMA. With the lazy max no p exceeds
