@@ -3,7 +3,10 @@
 ``python -m invariant_paged_kv_amd.build`` (or ``build_library()``) runs hipcc
 on ``csrc/plan.cpp`` and ``csrc/bia.hip``. Packed-fp32 instruction selection
 is turned off (``-packed-fp32-ops``); hipcc's host pass warns that it does not
-know the feature, which is harmless.
+know the feature, which is harmless. MFMAs are selected in their VGPR form
+(``-amdgpu-mfma-vgpr-form``): the latent kernels, which run one wave per SIMD
+with more than 256 registers, otherwise copy their output accumulators
+between the VGPR and AGPR files on every tile; no other kernel's code changes.
 """
 from __future__ import annotations
 
@@ -35,6 +38,7 @@ def compile_command(out: str = LIB_PATH) -> list:
     return [
         hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-shared", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
         *SOURCES, "-o", out,

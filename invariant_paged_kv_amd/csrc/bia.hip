@@ -1104,9 +1104,9 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
 //   K/V staging: the tile's two pages (16 rows x 1152 bytes each, contiguous
 //   in the pool) are copied to LDS by DMA, 18 instructions of 1 KB per page
 //   spread over the waves. LDS rows are unpadded; the 16-byte chunk c of
-//   tile row r sits at slot c ^ f(r), f(r) = (r / 2) % 8, which permutes
-//   chunks inside aligned groups of 8 and keeps the K-operand reads (16 rows,
-//   one chunk) and the transposing V reads on distinct banks. Four buffers:
+//   page row r sits at slot c ^ f(r) (mla_swz), which permutes chunks inside
+//   aligned groups of 8 and keeps the K-operand reads (16 rows, one chunk)
+//   and the transposing V reads on distinct banks. Four buffers:
 //   the DMAs of tiles j+1 .. j+3 are in flight while tile j computes, and a
 //   wave waits only for its own DMAs of tile j (counted waits). Keys past
 //   the partition's end read a valid key of the same page instead; their
@@ -1159,8 +1159,17 @@ __device__ __forceinline__ float quad_sum(float x) {
   return a + b;
 }
 
-// Slot of 16-byte chunk c in tile row r.
-__device__ __forceinline__ int mla_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Chunk permutation of page row r (0..15): chunk c sits at slot c ^ f(r),
+// f(r) = r % 8. Chosen by timing the two read patterns on gfx950 (eight
+// waves per CU reading at fixed per-lane offsets): the K reads (b128, 16
+// rows x one chunk) and the transposing V^T reads (rows 0..7 or 8..15, two
+// adjacent chunks) both run at the conflict-free rate with r % 8;
+// (r / 2) % 8 made the V^T reads 7 % slower and 2 ((r / 2) % 4) + r / 8
+// made the K reads 40 % slower. A row is 1152 bytes, so no swizzle leaves
+// every row on the same banks.
+__device__ __forceinline__ int mla_swz(int r) { return r & 7; }
+// Slot of 16-byte chunk c in page row r (an involution).
+__device__ __forceinline__ int mla_slot(int r, int c) { return c ^ mla_swz(r); }
 
 // Wait until at most n of this wave's DMAs are outstanding (n a multiple of
 // the per-tile count; vmcnt counts in issue order).
@@ -1219,8 +1228,14 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   // the DMAs are inline asm the compiler does not count, and a later
   // compiler wait for these loads would also wait for the DMAs.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Register placement (one wave per SIMD, 512 registers): the Q^T
+  // fragments, only ever MFMA operands, are held in AGPRs and the output
+  // accumulators in VGPRs (pinned after the PV MFMAs below). With the library
+  // built for VGPR-form MFMAs, the tile loop then moves nothing between the
+  // two files; left to itself the allocator kept O in VGPRs and copied all
+  // 128 registers into AGPRs and back around the PV MFMAs of every tile.
 #pragma unroll
-  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
+  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+a"(qf[s]));
   __syncthreads();
 
   // DMA of tile t into buffer t % 4: instruction i (0..17) of page half ph
@@ -1273,14 +1288,14 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
 
   // K operand of k-step s, key block kb: tile row 16 kb + n16 (f depends on
   // n16 only), chunk 4 s + g4 -> slot 8 (s / 2) + ((4 (s % 2) + g4) ^ f).
-  const int fk = (n16 >> 1) & 7;
+  const int fk = mla_swz(n16);
   const int k_off[2] = {n16 * kMlaRowBytes + 16 * ((0 + g4) ^ fk),
                         n16 * kMlaRowBytes + 16 * ((4 + g4) ^ fk)};
   // V^T operand of dim block b: rows 4 g4 + n16 / 4 (+ 16), dims 16 b + 4 (n16 % 4):
   // chunk 2 b + h (h = (n16 % 4) / 2), byte (n16 % 2) * 8 in it -> slot
   // 8 (b / 4) + ((2 (b % 4) + h) ^ f).
   const int vr = 4 * g4 + (n16 >> 2);
-  const int fv = (vr >> 1) & 7;
+  const int fv = mla_swz(vr);
   const int vh = (n16 & 3) >> 1;
   int v_off[4];
 #pragma unroll
@@ -1369,6 +1384,8 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
       if (b + kAhead < kMlaDv / 16) vf[(b + kAhead) % kRing] = vfrag(b + kAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b) asm volatile("" : "+v"(o[b]));  // O stays in VGPRs
   };
 
   // DMAs of tiles 0 .. 2 ahead of the loop; tile j+3 goes into the buffer of
@@ -1478,8 +1495,9 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
   for (int i = lane; i < n_tiles; i += 64) my_pages[i] = pt[i];  // one page per tile
   // Q and the page ids are waited for before any DMA is in flight.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  // Q^T fragments in AGPRs, O in VGPRs, as in mla_kernel.
 #pragma unroll
-  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
+  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+a"(qf[s]));
 
   // DMA of tile t: 18 instructions of 1 KB; instruction i, lane l copies LDS
   // bytes 1024 i + 16 l (row rr, slot sl) from chunk sl ^ f(rr) of row rr.
@@ -1501,13 +1519,13 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
     }
   };
 
-  const int fk = (n16 >> 1) & 7;
+  const int fk = mla_swz(n16);
   const int k_off[2] = {n16 * kMlaRowBytes + 16 * ((0 + g4) ^ fk),
                         n16 * kMlaRowBytes + 16 * ((4 + g4) ^ fk)};
   // V^T of dim block b: rows 4 g4 + n16 / 4 (the 4 keys of this lane group),
   // dims 16 b + 4 (n16 % 4) .. + 3
   const int vr = 4 * g4 + (n16 >> 2);
-  const int fv = (vr >> 1) & 7;
+  const int fv = mla_swz(vr);
   const int vh = (n16 & 3) >> 1;
   int v_off[4];
 #pragma unroll
@@ -1580,6 +1598,8 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
       if (b + kAhead < kMlaDv / 16) vf[(b + kAhead) % kRing] = vfrag(b + kAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 16; ++b) asm volatile("" : "+v"(o[b]));
   };
 
   issue(0);

@@ -70,6 +70,7 @@ def test_device_assembly_has_no_atomic_instructions(tmp_path):
     asm = str(tmp_path / "bia.s")
     cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            f"-I{INCLUDE}", f"-I{CSRC}", os.path.join(CSRC, "bia.hip"), "-o", asm]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
