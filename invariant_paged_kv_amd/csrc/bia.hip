@@ -1098,17 +1098,21 @@ decode_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q
 // averages its first 512 dims (the pages name this MLA path as the one with
 // no deterministic mode, sglang PR #43612, commit message and Summary).
 //
-// One workgroup = one WorkItem = 64 q rows (64 / hb tokens x hb heads of one
-// head block, hb = min(Hq, 64); the plan's "kv head" is the head block) over
-// one split-KV partition; 4 waves x 16 rows. Per 32-key tile:
+// One workgroup = one WorkItem = 128 q rows (128 / hb tokens x hb heads of
+// one head block, hb = min(Hq, 128); the plan's "kv head" is the head block)
+// over one split-KV partition; 8 waves x 16 rows, two waves per SIMD, so one
+// wave's softmax, waits and DMA issue overlap the other's MFMAs, and each K/V
+// tile staged in LDS serves 128 rows (at 128 heads, each latent row is read
+// once per token). Per 32-key tile:
 //   K/V staging: the tile's two pages (16 rows x 1152 bytes each, contiguous
 //   in the pool) are copied to LDS by DMA, 18 instructions of 1 KB per page
 //   spread over the waves. LDS rows are unpadded; the 16-byte chunk c of
 //   page row r sits at slot c ^ f(r) (mla_swz), which permutes chunks inside
 //   aligned groups of 8 and keeps the K-operand reads (16 rows, one chunk)
-//   and the transposing V reads on distinct banks. Four buffers:
-//   the DMAs of tiles j+1 .. j+3 are in flight while tile j computes, and a
-//   wave waits only for its own DMAs of tile j (counted waits). Keys past
+//   and the transposing V reads on distinct banks. Four buffers (147 KB,
+//   one workgroup per CU): the DMAs of tiles j+1 .. j+3 are in flight while
+//   tile j computes, and a wave waits only for its own DMAs of tile j
+//   (counted waits). Keys past
 //   the partition's end read a valid key of the same page instead; their
 //   scores are masked, so they add exact zeros. Page ids come from an LDS
 //   copy of the item's page list made once per item.
@@ -1138,7 +1142,9 @@ constexpr int kMlaPageBytes = 16 * kMlaRowBytes;        // 18432: one page
 constexpr int kMlaTileBytes = 2 * kMlaPageBytes;        // 36864
 constexpr int kMlaBufs = 4;
 constexpr int kMlaPageDma = kMlaPageBytes / 1024;       // 18 DMA instructions per page
-constexpr int kMlaDmaPerWave = (kMlaPageDma + 3) / 4;   // instructions i = wave + 4 k
+constexpr int kMlaWaves = 8;                            // two per SIMD
+constexpr int kMlaThreads = 64 * kMlaWaves;
+constexpr int kMlaDmaPerWave = (kMlaPageDma + kMlaWaves - 1) / kMlaWaves;  // i = wave + 8 k
 constexpr int kMlaMaxPages = BIA_MLA_MAX_SPLIT / 16;    // page list held in LDS
 static_assert(kMlaPageBytes % 1024 == 0, "a page is whole DMA instructions");
 
@@ -1176,14 +1182,14 @@ __device__ __forceinline__ int mla_slot(int r, int c) { return c ^ mla_swz(r); }
 __device__ __forceinline__ void mla_wait(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
     case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
   }
 }
 
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kMlaThreads, 1)
 mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
            const uint16_t* __restrict__ kvp, const int32_t* __restrict__ page_table,
            float scale_log2, int num_qo_heads, int hb_shift, int split,
@@ -1199,7 +1205,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   const int g4 = lane >> 4;   // 16-lane group
   const int n16 = lane & 15;  // the lane's row among the wave's 16 (and its M index)
   const int hb = 1 << hb_shift;
-  const int x = wave * 16 + n16;  // row of the 64-row tile
+  const int x = wave * 16 + n16;  // row of the 128-row tile
   const int tok = x >> hb_shift;
   const int hq = it.kv_head * hb + (x & (hb - 1));
   const bool row_valid = tok < it.n_tok;
@@ -1223,40 +1229,40 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   const int first_page = it.kv_begin >> 4;
   const int n_pages = ((kv_end - 1) >> 4) - first_page + 1;  // <= kMlaMaxPages (plan check)
   const int32_t* pt = page_table + it.page_off + first_page;
-  for (int i = tid; i < n_pages; i += kThreads) lds_pages[i] = pt[i];
+  for (int i = tid; i < n_pages; i += kMlaThreads) lds_pages[i] = pt[i];
   // Q and the page list are waited for here, before any DMA is in flight:
   // the DMAs are inline asm the compiler does not count, and a later
   // compiler wait for these loads would also wait for the DMAs.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // Register placement (one wave per SIMD, 512 registers): the Q^T
+  // Register placement (two waves per SIMD, 256 registers each): the Q^T
   // fragments, only ever MFMA operands, are held in AGPRs and the output
   // accumulators in VGPRs (pinned after the PV MFMAs below). With the library
   // built for VGPR-form MFMAs, the tile loop then moves nothing between the
   // two files; left to itself the allocator kept O in VGPRs and copied all
   // 128 registers into AGPRs and back around the PV MFMAs of every tile.
 #pragma unroll
-  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+a"(qf[s]));
+  for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
   __syncthreads();
 
   // DMA of tile t into buffer t % 4: instruction i (0..17) of page half ph
   // copies LDS bytes ph * 18432 + 1024 i + 16 lane .. + 15 of the tile, which
   // hold tile row r = 16 ph + (1024 i + 16 lane) / 1152 at slot
   // ((1024 i + 16 lane) % 1152) / 16 = mla_slot(r, c) for chunk c. Wave w
-  // issues i = w, w + 4, ..: 10 instructions per tile for waves 0-1, 8 for
-  // waves 2-3 (the same count for every tile, ragged ones included).
+  // issues i = w, w + 8, ..: 6 instructions per tile for waves 0-1, 4 for
+  // waves 2-7 (the same count for every tile, ragged ones included).
   const uint32_t lds_base = lds_offset(lds);
   uint32_t dma_off[kMlaDmaPerWave];  // byte offset of this lane's chunk in its page
   int dma_row[kMlaDmaPerWave];       // its row in the page
 #pragma unroll
   for (int k = 0; k < kMlaDmaPerWave; ++k) {
-    const int i = wave + 4 * k;
+    const int i = wave + kMlaWaves * k;
     const int p = 1024 * i + 16 * lane;
     const int rr = p / kMlaRowBytes;
     const int c = mla_slot(rr, (p % kMlaRowBytes) / 16);  // the slot map is an involution
     dma_row[k] = rr;
     dma_off[k] = static_cast<uint32_t>(rr * kMlaRowBytes + c * 16);
   }
-  const int dma_count = 2 * ((kMlaPageDma - wave + 3) / 4);  // 10 or 8 per tile
+  const int dma_count = 2 * ((kMlaPageDma - wave + kMlaWaves - 1) / kMlaWaves);  // 6 or 4
   auto issue = [&](int t) {
     const int t0 = it.kv_begin + kMlaKeys * t;
     const bool ragged = t0 + kMlaKeys > kv_end;
@@ -1269,7 +1275,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
       const uint32_t buf_lds = lds_base + (t % kMlaBufs) * kMlaTileBytes + ph * kMlaPageBytes;
 #pragma unroll
       for (int k = 0; k < kMlaDmaPerWave; ++k) {
-        const int i = wave + 4 * k;
+        const int i = wave + kMlaWaves * k;
         if (i < kMlaPageDma) {  // wave-uniform
           uint32_t off = dma_off[k];
           if (ragged && t0 + 16 * ph + dma_row[k] >= kv_end)  // past the keys: a valid key's chunk
@@ -1303,7 +1309,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     v_off[b4] = vr * kMlaRowBytes + 16 * ((2 * b4 + vh) ^ fv) + 8 * (n16 & 1);
 
   // A wave whose rows are all past the item's tokens (decode with fewer than
-  // 64 rows, a request's last tile) skips the MFMAs; it still issues its DMAs
+  // 128 rows, a request's last tile) skips the MFMAs; it still issues its DMAs
   // and meets every barrier.
   const bool wave_active = ((wave * 16) >> hb_shift) < it.n_tok;
   auto compute = [&](int j, int buf) {
@@ -1312,7 +1318,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     // ---- scores: S^T for keys 16 kb + m (m = n16) x the wave's 16 rows ----
     // MFMA i = 2 s + kb; its K fragment is read kAhead MFMAs earlier (ring of
     // kRing registers), each slot fenced so the reads stay ahead.
-    constexpr int kAhead = 6, kRing = 8, kNs = 2 * (kMlaDk / 32);
+    constexpr int kAhead = 4, kRing = 6, kNs = 2 * (kMlaDk / 32);
     auto kfrag = [&](int i) -> bf16x8 {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
                                             base + (i & 1) * kMlaPageBytes +
@@ -2333,7 +2339,7 @@ bia_status run_mla(const bia_plan* plan, bia_mode mode, const void* q, const voi
                        page_table_dev, sm_scale * kLog2e, d.num_qo_heads, d.group, d.split, o,
                        lse, L.o_part, L.lse_part);
   } else {
-    hipLaunchKernelGGL(mla_kernel, dim3(L.n), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(mla_kernel, dim3(L.n), dim3(kMlaThreads), 0, stream,
                        reinterpret_cast<const WorkItem*>(L.items), static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(kv_pool), page_table_dev, sm_scale * kLog2e,
                        d.num_qo_heads, hb_shift, d.split, o, lse, L.o_part, L.lse_part);

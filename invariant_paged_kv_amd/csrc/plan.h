@@ -47,7 +47,7 @@ static_assert(sizeof(AppendItem) == 16, "append item is 4 int32");
 static_assert(sizeof(MergeItem) == 32, "merge item is 8 int32");
 
 constexpr int kQTileRows = BIA_Q_TILE_ROWS;
-constexpr int kMlaTileRows = 64;  // q rows of one latent-attention work item
+constexpr int kMlaTileRows = 128;  // q rows of one latent-attention work item
 constexpr int kKvTile = BIA_KV_TILE;
 constexpr int kPageSize = BIA_PAGE_SIZE;
 constexpr size_t kWsAlign = 256;

@@ -177,13 +177,13 @@ def test_mla_plan_without_flag_rejects_576():
 
 @pytest.mark.parametrize("hq", [16, 128])
 def test_mla_items_cover_every_head_and_token(hq):
-    """Items of a latent plan: 64-row tiles of 64 / min(Hq, 64) tokens, one
+    """Items of a latent plan: 128-row tiles of 128 / min(Hq, 128) tokens, one
     per head block, so every (token, q head) row sits in exactly one tile of
     each partition it needs; partial states hold 512 dims."""
     p = plan(qo=(0, 100, 400), kv=(0, 100, 700), heads=dict(num_qo_heads=hq, **MLA),
              flags=bia.BIA_PLAN_MLA, split=256)
-    hb = min(hq, 64)
-    T = 64 // hb
+    hb = min(hq, 128)
+    T = 128 // hb
     its = items_of(p)
     assert max(it["n_tok"] for it in its) == T
     assert {it["kv_head"] for it in its} == set(range(hq // hb))
