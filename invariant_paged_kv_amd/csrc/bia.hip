@@ -1655,13 +1655,17 @@ merge_tiles_kernel(const MergeItem* __restrict__ merges, const float* __restrict
                    const float* __restrict__ lse_part, int num_qo_heads, int group_shift,
                    uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int TPR = D / 4;              // threads per row
-  constexpr int RPP = kThreads / TPR;     // rows per pass
+  constexpr int RPB = kThreads / TPR;     // rows per workgroup
   const MergeItem mi = merges[blockIdx.x];
   const int g = 1 << group_shift;
   const int rows = mi.n_tok * g;
   const int d0 = (threadIdx.x % TPR) * 4;
   constexpr int kBatch = 8;  // states loaded ahead of their fold
-  for (int x = threadIdx.x / TPR; x < rows; x += RPP) {
+  // workgroup (i, c) takes rows c RPB .. c RPB + RPB - 1 of merge item i, so
+  // an item's rows spread over the chip (a 128-head latent decode is one
+  // 128-row item per request)
+  const int x = blockIdx.y * RPB + threadIdx.x / TPR;
+  if (x < rows) {
     float M = kNegInf, sum = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int k0 = 0; k0 < mi.n_splits; k0 += kBatch) {
       // issue the loads of up to kBatch states, then fold them in order
@@ -2028,7 +2032,12 @@ __global__ void __launch_bounds__(kThreads) upload_kernel(const uint4* __restric
     dst[i] = src[i];
 }
 
-int log2_exact(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
+// log2 of a power-of-two group (GQA 1..8, latent head blocks up to 128)
+int log2_exact(int g) {
+  int s = 0;
+  while ((1 << s) < g) ++s;
+  return s;
+}
 
 bia_status check_run(const bia_plan* plan, bia_mode mode, bool mla, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* page_table_dev, float sm_scale,
@@ -2110,11 +2119,20 @@ ListLaunch plan_merges(const bia::PlanData& d, unsigned char* ws) {
   return L;
 }
 
+// max_rows bounds the rows of one merge item: a prefill tile (tile tokens
+// x group) or one decode token's group.
 template <int D>
-void launch_merge_tiles(const ListLaunch& L, uint16_t* out, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_tiles_kernel<D>, dim3(L.n), dim3(kThreads), 0, stream,
+void launch_merge_tiles(const ListLaunch& L, int max_rows, uint16_t* out, float* lse,
+                        hipStream_t stream) {
+  constexpr int RPB = kThreads / (D / 4);
+  const unsigned chunks = static_cast<unsigned>((max_rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL(merge_tiles_kernel<D>, dim3(L.n, chunks), dim3(kThreads), 0, stream,
                      reinterpret_cast<const MergeItem*>(L.items), L.o_part, L.lse_part,
                      L.num_qo_heads, log2_exact(L.group), out, lse);
+}
+
+int merge_rows(const bia::PlanData& d) {
+  return (d.mode == BIA_MODE_DECODE ? 1 : d.tile_tokens) * d.group;
 }
 
 template <int D, int G>
@@ -2203,9 +2221,9 @@ extern "C" bia_status bia_prefill_paged(const bia_plan* plan, const void* q, con
   }
   if (!d.merges.empty()) {
     if (d.head_dim == 128)
-      launch_merge_tiles<128>(plan_merges(d, ws), o, lse, stream);
+      launch_merge_tiles<128>(plan_merges(d, ws), merge_rows(d), o, lse, stream);
     else
-      launch_merge_tiles<64>(plan_merges(d, ws), o, lse, stream);
+      launch_merge_tiles<64>(plan_merges(d, ws), merge_rows(d), o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -2238,9 +2256,9 @@ bia_status run_decode(const bia_plan* plan, const void* q, const void* k_pool,
                         stream);
   if (!d.merges.empty()) {
     if (d.head_dim == 128)
-      launch_merge_tiles<128>(plan_merges(d, ws), o, lse, stream);
+      launch_merge_tiles<128>(plan_merges(d, ws), merge_rows(d), o, lse, stream);
     else
-      launch_merge_tiles<64>(plan_merges(d, ws), o, lse, stream);
+      launch_merge_tiles<64>(plan_merges(d, ws), merge_rows(d), o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -2345,10 +2363,7 @@ bia_status run_mla(const bia_plan* plan, bia_mode mode, const void* q, const voi
                        d.num_qo_heads, hb_shift, d.split, o, lse, L.o_part, L.lse_part);
   }
   if (!d.merges.empty()) {
-    const ListLaunch M = plan_merges(d, ws);
-    hipLaunchKernelGGL(merge_tiles_kernel<kMlaDv>, dim3(M.n), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const MergeItem*>(M.items), M.o_part, M.lse_part,
-                       M.num_qo_heads, hb_shift, o, lse);
+    launch_merge_tiles<kMlaDv>(plan_merges(d, ws), merge_rows(d), o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "MLA launch");
@@ -2484,9 +2499,9 @@ extern "C" bia_status bia_decode_graph_run(const bia_decode_graph* dg, int32_t b
     L.items = ws + d.off_merges;
     L.n = static_cast<unsigned>(int64_t(batch) * d.num_kv_heads);
     if (d.head_dim == 128)
-      launch_merge_tiles<128>(L, o, lse, stream);
+      launch_merge_tiles<128>(L, d.group, o, lse, stream);
     else
-      launch_merge_tiles<64>(L, o, lse, stream);
+      launch_merge_tiles<64>(L, d.group, o, lse, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode graph launch");
