@@ -1318,7 +1318,7 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     // ---- scores: S^T for keys 16 kb + m (m = n16) x the wave's 16 rows ----
     // MFMA i = 2 s + kb; its K fragment is read kAhead MFMAs earlier (ring of
     // kRing registers), each slot fenced so the reads stay ahead.
-    constexpr int kAhead = 4, kRing = 6, kNs = 2 * (kMlaDk / 32);
+    constexpr int kAhead = 3, kRing = 4, kNs = 2 * (kMlaDk / 32);
     auto kfrag = [&](int i) -> bf16x8 {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
                                             base + (i & 1) * kMlaPageBytes +
