@@ -1234,12 +1234,12 @@ mla_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
   // the DMAs are inline asm the compiler does not count, and a later
   // compiler wait for these loads would also wait for the DMAs.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // Register placement (two waves per SIMD, 256 registers each): the Q^T
-  // fragments, only ever MFMA operands, are held in AGPRs and the output
-  // accumulators in VGPRs (pinned after the PV MFMAs below). With the library
-  // built for VGPR-form MFMAs, the tile loop then moves nothing between the
-  // two files; left to itself the allocator kept O in VGPRs and copied all
-  // 128 registers into AGPRs and back around the PV MFMAs of every tile.
+  // Register placement (two waves per SIMD, 256 registers each): Q^T, O
+  // and everything else in VGPRs, none in AGPRs. With the library built for
+  // VGPR-form MFMAs the tile loop moves nothing between the two register
+  // files (an even VGPR/AGPR split at this occupancy spilled, and at one wave
+  // per SIMD the allocator copied the 128 O registers between the files
+  // around the PV MFMAs of every tile).
 #pragma unroll
   for (int s = 0; s < kMlaDk / 32; ++s) asm volatile("" : "+v"(qf[s]));
   __syncthreads();

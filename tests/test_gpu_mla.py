@@ -88,7 +88,7 @@ def test_mla_decode_parity(hq):
 
 
 def test_mla_many_partitions_hq32():
-    """32 q heads (two tokens per 64-row tile) at split 64: rows span up to
+    """32 q heads (four tokens per 128-row tile) at split 64: rows span up to
     ten partitions, merged in fixed order at 512 dims; ragged lengths."""
     reqs = [W.Request(67, 600, 981), W.Request(3, 64, 982), W.Request(1, 65, 983),
             W.Request(130, 130, 984)]
@@ -230,7 +230,7 @@ def test_mla_rising_logits(hq):
     """Latent logits that climb along the sequence: rows raise their running
     max mid-row again and again; the 1500-key request spans partitions whose
     states merge with very different lse. Decode covers the one-wave kernel
-    (16 heads) and the 64-row kernel (128 heads)."""
+    (16 heads) and the 128-row kernel (128 heads)."""
     say(f"mla rising logits hq={hq}")
     b = W.rising_mla_batch([400, 200, 9], [400, 1500, 9], num_qo_heads=hq, seed=91,
                            num_pages=256, rise=1.5, device=DEV)
