@@ -75,16 +75,30 @@ def test_mla_prefill_parity(hq, split):
     mla_parity(b, out, lse, f"mla prefill hq={hq} split={split}")
 
 
-@pytest.mark.parametrize("hq", [16, 128])
+@pytest.mark.parametrize("hq", [16, 32, 64, 128])
 def test_mla_decode_parity(hq):
     """One query token per request; lengths around and past the 2048-key
-    decode split."""
+    decode split. 16 heads take the one-wave-per-item kernel; 32 and 64 the
+    128-row kernel with two and four of its eight waves holding rows."""
     kv = [1, 17, 2048, 2049, 5000]
     reqs = [W.Request(1, c, 920 + i) for i, c in enumerate(kv)]
     say(f"mla decode parity hq={hq}")
     b = W.make_mla_batch(reqs, num_qo_heads=hq, num_pages=1024, batch_seed=43, device=DEV)
     out, lse = run_mla(b, mode=bia.BIA_MODE_DECODE)
     mla_parity(b, out, lse, f"mla decode hq={hq}")
+
+
+@pytest.mark.parametrize("hq", [8, 64])
+def test_mla_prefill_parity_tile_tokens(hq):
+    """128-row tiles hold 128 / min(Hq, 128) tokens: 16 at 8 heads, 2 at 64.
+    Token counts that are not multiples of that (a request's last tile
+    partly empty), a one-token request and a chunk starting mid-sequence."""
+    reqs = [W.Request(37, 300, 951), W.Request(1, 1, 952), W.Request(17, 17, 953),
+            W.Request(5, 129, 954)]
+    say(f"mla prefill tile tokens hq={hq}")
+    b = W.make_mla_batch(reqs, num_qo_heads=hq, num_pages=128, batch_seed=75, device=DEV)
+    out, lse = run_mla(b, split=256)
+    mla_parity(b, out, lse, f"mla prefill hq={hq} split=256")
 
 
 def test_mla_many_partitions_hq32():
@@ -185,9 +199,9 @@ def test_mla_decode_batch_invariance_hq16():
             assert bits_equal(o, ref[0]) and bits_equal(l, ref[1]), n
 
 
-@pytest.mark.parametrize("hq", [128])
+@pytest.mark.parametrize("hq", [32, 64, 128])
 def test_mla_decode_equals_prefill_last_row(hq):
-    """With 64 or more q heads, decode runs the prefill kernel on a one-token
+    """With 32 or more q heads, decode runs the prefill kernel on a one-token
     tile, so it equals the last row of the request's prefill at the same
     split bit for bit (the row's arithmetic does not depend on its tile).
     With 16 or fewer heads decode takes 16-key tiles of its own and is only
