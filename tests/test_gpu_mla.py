@@ -88,6 +88,25 @@ def test_mla_decode_parity(hq):
     mla_parity(b, out, lse, f"mla decode hq={hq}")
 
 
+@pytest.mark.parametrize("split", [8192, 16384])
+def test_mla_large_splits(split):
+    """Splits above 2048 up to the largest allowed (16384): 16-head decode
+    then runs the 128-row kernel instead of the one-wave-per-item one, and
+    the prefill items of a 64-token chunk over a 12000-token prefix loop over
+    up to 375 32-key tiles, with rows spanning one or two partitions."""
+    kv = [1, 2049, 9000, 17000]
+    reqs = [W.Request(1, c, 960 + i) for i, c in enumerate(kv)]
+    say(f"mla decode hq=16 split={split}")
+    b = W.make_mla_batch(reqs, num_qo_heads=16, num_pages=2048, batch_seed=47, device=DEV)
+    out, lse = run_mla(b, mode=bia.BIA_MODE_DECODE, split=split)
+    mla_parity(b, out, lse, f"mla decode hq=16 split={split}")
+    reqs = [W.Request(64, 12000, 965), W.Request(64, 64, 966)]
+    say(f"mla prefill hq=16 split={split}")
+    b = W.make_mla_batch(reqs, num_qo_heads=16, num_pages=1024, batch_seed=48, device=DEV)
+    out, lse = run_mla(b, split=split)
+    mla_parity(b, out, lse, f"mla prefill hq=16 split={split}")
+
+
 @pytest.mark.parametrize("hq", [8, 64])
 def test_mla_prefill_parity_tile_tokens(hq):
     """128-row tiles hold 128 / min(Hq, 128) tokens: 16 at 8 heads, 2 at 64.
