@@ -476,13 +476,21 @@ def main():
     d_lse = torch.empty(db.q.shape[:2], dtype=torch.float32, device=dev)
     heads = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128)
 
-    def make_plans():
+    plan_s = {"prefill": [], "decode": []}
+
+    def make_plans(timed=False):
+        t0 = time.perf_counter()
         pp = bia.bia_plan_create(bia.BIA_MODE_PREFILL, pb.qo_indptr, pb.kv_indptr,
                                  pb.page_table, num_pages=pb.num_pages,
                                  split_size=bia.BIA_PREFILL_SPLIT, **heads)
+        t1 = time.perf_counter()
         dp = bia.bia_plan_create(bia.BIA_MODE_DECODE, db.qo_indptr, db.kv_indptr,
                                  db.page_table, num_pages=db.num_pages,
                                  split_size=bia.BIA_DECODE_SPLIT, **heads)
+        t2 = time.perf_counter()
+        if timed:
+            plan_s["prefill"].append(t1 - t0)
+            plan_s["decode"].append(t2 - t1)
         return pp, dp
 
     pp, dp = make_plans()
@@ -494,7 +502,7 @@ def main():
     p_timer, d_timer = Timer(torch, stream), Timer(torch, stream)
 
     def step(timed: bool):
-        pp, dp = make_plans()                      # a1: plan from the lengths alone
+        pp, dp = make_plans(timed)                 # a1: plan from the lengths alone
         s = p_timer.start() if timed else None
         bia.bia_prefill_paged(pp, pb.q, pb.k_pool, pb.v_pool, p_pt, pb.sm_scale, p_out,
                               p_lse, p_ws, stream)
@@ -581,6 +589,11 @@ def main():
             },
         },
         "bit_invariant_across_steps": invariant,
+        "plan_ms": {
+            "prefill": round(float(np.median(plan_s["prefill"])) * 1e3, 4),
+            "decode": round(float(np.median(plan_s["decode"])) * 1e3, 4),
+            "what": "host time of bia_plan_create (median over the timed steps), "
+                    "included in ms_per_step, not in the GPU call timings"},
     }
     if extras:
         copy = extras["copy_gbs"]
