@@ -770,8 +770,9 @@ prefill_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one workgroup = one WorkItem = (request, kv head, partition of up to
-// `split` keys), g q heads. The partition's keys go in 16-key chunks to the 4
+// Decode on the VALU (head_dim 64, and splits past the MFMA decode's page
+// list; head_dim 128 runs decode_mfma_kernel below): one workgroup = one
+// WorkItem = (request, kv head, partition of up to `split` keys), g q heads. The partition's keys go in 16-key chunks to the 4
 // waves round-robin (chunk c -> wave c % 4). In a wave, 8 lanes share one key
 // (each holds D/8 of its dims, so 16-byte loads read whole rows) and a lane
 // group takes keys c*16 + ks and c*16 + 8 + ks (one page). Chunks rotate
@@ -1644,6 +1645,242 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
 }
 
 // ---------------------------------------------------------------------------
+// a4 on MFMA: decode with D = 128 (decode_mfma_kernel<G>). One workgroup of
+// four waves runs one item (request, kv head, partition); the partition's
+// 16-key tiles (one page each) go round-robin to the waves, tile t to wave
+// t % 4, and each wave keeps its own online-softmax state. Per tile and wave:
+//   K and V rows of the kv head reach the wave's LDS buffers by DMA (4 + 4
+//   instructions of 1 KB), NB buffers deep, counted waits;
+//   S^T = K Q^T: 4 v_mfma_f32_16x16x32_bf16, keys as M, the group's G q heads
+//   as N (16 columns, G of them real);
+//   online softmax per q head over the lanes n, n + 16, n + 32, n + 48;
+//   O^T += V^T P^T: 8 v_mfma_f32_16x16x16_bf16, P as the scores left it,
+//   V^T by transposing reads.
+// The four waves' states fold in ascending wave order (combine_sym), as in
+// decode_kernel. The page list of the partition is copied to LDS once, so the
+// tile loop holds no global load the compiler would count.
+// ---------------------------------------------------------------------------
+constexpr int kDecMfmaWaves = 4;
+constexpr int kDecMfmaMaxPages = 1024;  // page list in LDS: splits up to 16384 keys
+constexpr int kDecMfmaBufs = 2;         // tile buffers per wave
+
+// Chunk permutation of tile row r (16 chunks of 16 bytes): chunk c sits at
+// slot c ^ f(r), f(r) = 2 (r % 8) + r / 8. The K reads (row n16, one chunk,
+// 16 rows per 16 lanes) then take 16 distinct slots of a 256-byte bank cycle,
+// and the transposing V reads (rows 4 g4 .. 4 g4 + 3, 32 bytes each, and any
+// 8 consecutive rows) take distinct 32-byte halves of it.
+__device__ __forceinline__ int dec_swz(int r) { return ((r & 7) << 1) | (r >> 3); }
+
+template <int N>
+__device__ __forceinline__ void dec_wait(int tiles_ahead) {
+  // N DMA instructions per tile; tiles_ahead (0 .. 2) tiles may stay in flight
+  if (tiles_ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * N) : "memory");
+  else if (tiles_ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int G>
+__global__ void __launch_bounds__(64 * kDecMfmaWaves, 2)
+decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
+                   const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+                   const int32_t* __restrict__ page_table, float scale_log2, int num_qo_heads,
+                   int num_kv_heads, int split, uint16_t* __restrict__ out,
+                   float* __restrict__ lse_out, float* __restrict__ o_part,
+                   float* __restrict__ lse_part) {
+  constexpr int D = 128;
+  constexpr int RB = 2 * D;        // bytes of one key row of one head
+  constexpr int TB = 16 * RB;      // one tensor's tile: 16 keys, 4 KB
+  constexpr int NI = TB / 1024;    // DMA instructions per tensor tile
+  constexpr int NS = D / 32;       // score k-steps
+  constexpr int NV = D / 16;       // PV dim blocks
+  constexpr int NB = kDecMfmaBufs;
+  static_assert(kDecMfmaWaves * NB * 2 * TB >= kDecMfmaWaves * (G * D + 2 * G) * 4,
+                "the wave states fit in the tile buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDecMfmaWaves][NB][2 * TB];
+  __shared__ int32_t lds_pages[kDecMfmaMaxPages];
+
+  const WorkItem it = items[blockIdx.x];
+  if (it.n_tok == 0) return;  // a fixed-capacity slot past the request's partitions
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;       // q head kv_head * G + n16 when n16 < G
+  const bool row_valid = n16 < G;
+
+  const int kv_end = min(it.kv_begin + split, it.kv_len);
+  const int n_tiles = (kv_end - it.kv_begin + 15) >> 4;
+  const int32_t* pt = page_table + it.page_off + (it.kv_begin >> 4);
+  for (int i = tid; i < n_tiles; i += 64 * kDecMfmaWaves) lds_pages[i] = pt[i];
+
+  // Q^T fragments (B operand): q head n16, dims 32 s + 8 g4 .. + 7; zero for
+  // the columns past the group
+  const int64_t q_row = static_cast<int64_t>(it.q_row0) * num_qo_heads + it.kv_head * G +
+                        (row_valid ? n16 : 0);
+  bf16x8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row_valid) w = *reinterpret_cast<const uint4*>(q + q_row * D + 32 * s + 8 * g4);
+    qf[s] = __builtin_bit_cast(bf16x8, w);
+  }
+  // q and the page list are waited for before any DMA is in flight
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // DMA of tile t into buffer b: tensor x, instruction i fills rows 4 i ..
+  // 4 i + 3 of the buffer's x half; lane l puts 16 bytes in slot l % 16 of
+  // row 4 i + l / 16, i.e. chunk (l % 16) ^ f(row) of that key's row. Keys
+  // past the partition read its last key (same page: tiles are page-aligned).
+  const uint32_t lds_base = lds_offset(&lds[wave][0][0]);
+  const int64_t slot_bytes = static_cast<int64_t>(num_kv_heads) * RB;
+  const int64_t head_bytes = static_cast<int64_t>(it.kv_head) * RB;
+  const int last_key = kv_end - 1;
+  auto issue = [&](int t, int b) {
+    const int32_t page = __builtin_amdgcn_readfirstlane(lds_pages[t]);
+    const int64_t page_bytes = static_cast<int64_t>(page) * 16 * slot_bytes + head_bytes;
+    const int t0 = it.kv_begin + 16 * t;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(x == 0 ? kp : vp) + page_bytes;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int key = min(t0 + r, last_key);
+        const uint32_t off =
+            static_cast<uint32_t>((key & 15) * slot_bytes + 16 * ((lane & 15) ^ dec_swz(r)));
+        lds_dma16_sbase(off, base, lds_base + b * (2 * TB) + x * TB + 1024 * i);
+      }
+    }
+  };
+
+  // K fragment s (A operand): key n16, dims 32 s + 8 g4 .., chunk 4 s + g4
+  const int fk = dec_swz(n16);
+  // V^T fragment of dim block b: keys 4 g4 .. 4 g4 + 3 (row vr and the three
+  // after it, transposed by the read), dims 16 b + 4 (n16 % 4) .. + 3
+  const int vr = 4 * g4 + (n16 >> 2);
+  const int fv = dec_swz(vr);
+
+  float m = kNegInf;
+  float lsum = 0.0f;
+  f32x4 o[NV];
+#pragma unroll
+  for (int b = 0; b < NV; ++b) o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int t, int b) {
+    const uint8_t* kb = &lds[wave][b][0];
+    const uint8_t* vb = kb + TB;
+    bf16x8 kf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[s] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(kb + n16 * RB + 16 * ((4 * s + g4) ^ fk)));
+    v4i16_t vf[NV];
+#pragma unroll
+    for (int d = 0; d < NV; ++d)
+      vf[d] = __builtin_bit_cast(
+          v4i16_t, lds_read_tr16(vb + vr * RB + 16 * ((2 * d + ((n16 & 3) >> 1)) ^ fv) +
+                                 8 * (n16 & 1)));
+    f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
+    // lane (n16, g4) holds keys t0 + 4 g4 .. + 3 of q head n16
+    const int t0 = it.kv_begin + 16 * t;
+    if (t0 + 16 > kv_end) {  // the partition's last, partly filled tile
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = (t0 + 4 * g4 + v < kv_end) ? sc[v] : kNegInf;
+    }
+    if (!row_valid) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = kNegInf;
+    }
+    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float mt = quad_max(mx) * scale_log2;
+    const bool raise = mt > m + kLazyMax;
+    const float m_new = raise ? mt : m;
+    const float alpha = raise ? fast_exp2(m - m_new) : 1.0f;
+    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+    float p[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[v] = fast_exp2(__builtin_fmaf(sc[v], scale_log2, neg_m));
+      psum += p[v];
+    }
+    const v4i16_t pw = __builtin_bit_cast(
+        v4i16_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+    if (__any(raise)) {  // lanes whose q head did not raise have alpha == 1
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < NV; ++d) o[d] *= alpha;
+    }
+    lsum += psum;
+    m = m_new;
+#pragma unroll
+    for (int d = 0; d < NV; ++d)
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[d], pw, o[d], 0, 0, 0);
+  };
+
+  // this wave's tiles: wave, wave + 4, ...; NB in flight, each sent into the
+  // buffer the tile before it has finished with
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kDecMfmaWaves - 1) / kDecMfmaWaves : 0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+    if (k < my_tiles) issue(wave + kDecMfmaWaves * k, k);
+  for (int k = 0; k < my_tiles; ++k) {
+    dec_wait<2 * NI>(min(NB - 1, my_tiles - 1 - k));  // tile k has landed
+    compute(wave + kDecMfmaWaves * k, k % NB);         // its LDS reads are done on return
+    if (k + NB < my_tiles) issue(wave + kDecMfmaWaves * (k + NB), k % NB);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- fold the four waves' states in order (their buffers are free now) ----
+  const float l_row = quad_sum(lsum);
+  __syncthreads();  // every wave is past its last tile
+  float* sm_o = reinterpret_cast<float*>(&lds[0][0][0]);  // [wave][G][D]
+  float* sm_ml = sm_o + kDecMfmaWaves * G * D;             // [wave][G][2]
+  if (row_valid) {
+#pragma unroll
+    for (int d = 0; d < NV; ++d)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sm_o[(wave * G + n16) * D + 16 * d + 4 * g4 + v] = o[d][v];
+    if (g4 == 0) {
+      sm_ml[(wave * G + n16) * 2] = m;
+      sm_ml[(wave * G + n16) * 2 + 1] = l_row;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 64 * kDecMfmaWaves) {
+    const int j = e / D;
+    const int d = e % D;
+    float mm = sm_ml[j * 2], ll = sm_ml[j * 2 + 1];
+    float oo[1] = {sm_o[j * D + d]};
+#pragma unroll
+    for (int w = 1; w < kDecMfmaWaves; ++w) {
+      const float o2[1] = {sm_o[(w * G + j) * D + d]};
+      combine_sym<1>(mm, ll, oo, sm_ml[(w * G + j) * 2], sm_ml[(w * G + j) * 2 + 1], o2);
+    }
+    float lse_nat = kNegInf;
+    float val = 0.0f;
+    if (ll > 0.0f) {
+      val = oo[0] * (1.0f / ll);
+      lse_nat = (mm + fast_log2(ll)) * kLn2;
+    }
+    const int h = it.kv_head * G + j;
+    if (it.state < 0) {
+      out[(static_cast<int64_t>(it.q_row0) * num_qo_heads + h) * D + d] = to_bf16_bits(val);
+      if (lse_out != nullptr && d == 0)
+        lse_out[static_cast<int64_t>(it.q_row0) * num_qo_heads + h] = lse_nat;
+    } else {
+      const int64_t st = static_cast<int64_t>(it.state) + j;
+      o_part[st * D + d] = val;
+      if (d == 0) lse_part[st] = lse_nat;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of a tile's partitions (prefill rows spanning several partitions,
 // decode requests longer than one partition): row x of MergeItem mi folds
 // slots state0 + k * stride + x, k ascending, with fold_state. D/4 threads
@@ -2150,10 +2387,30 @@ void launch_decode(const ListLaunch& L, const uint16_t* q, const uint16_t* kp, c
                      L.num_qo_heads, L.num_kv_heads, L.split, out, lse, L.o_part, L.lse_part);
 }
 
+template <int G>
+void launch_decode_mfma(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
+                        const uint16_t* vp, const int32_t* pt, float scale_log2, uint16_t* out,
+                        float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mfma_kernel<G>), dim3(L.n), dim3(64 * kDecMfmaWaves), 0, stream,
+                     reinterpret_cast<const WorkItem*>(L.items), q, kp, vp, pt, scale_log2,
+                     L.num_qo_heads, L.num_kv_heads, L.split, out, lse, L.o_part, L.lse_part);
+}
+
 template <int D>
 void launch_decode_g(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
                      const uint16_t* vp, const int32_t* pt, float scale_log2, uint16_t* out,
                      float* lse, hipStream_t stream) {
+  // D = 128 at splits the LDS page list holds: the MFMA decode (the choice
+  // depends on the head dim and the split only, never on the batch)
+  if (D == 128 && L.split <= 16 * kDecMfmaMaxPages) {
+    switch (L.group) {
+      case 1: launch_decode_mfma<1>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      case 2: launch_decode_mfma<2>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      case 4: launch_decode_mfma<4>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      default: launch_decode_mfma<8>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+    }
+    return;
+  }
   switch (L.group) {
     case 1: launch_decode<D, 1>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
     case 2: launch_decode<D, 2>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;

@@ -8,9 +8,11 @@ tolerance.
   tile loop runs up to 256 tiles, rows that span two partitions (8192) or
   one (16384, written directly without a merge), next to a request with no
   prefix.
-* Decode at splits 64, 1024, 4096 and 16384 over contexts from 1 to 17000
-  keys: up to 266 partition states folded per request (split 64), and
-  requests that fit in one partition at the larger splits."""
+* Decode at splits 64, 1024, 4096, 16384 and 32768 over contexts from 1 to
+  17000 keys: up to 266 partition states folded per request (split 64), and
+  requests that fit in one partition at the larger splits. Up to 16384 the
+  decode runs on MFMA; 32768 is past its page list and runs the VALU decode
+  at the same head dim."""
 import pytest
 
 import workloads as W
@@ -30,7 +32,7 @@ def test_prefill_large_splits(split):
     assert_parity(out, lse, b, reqs=[0, 1], local_rows=rows, what=f"prefill split {split}")
 
 
-@pytest.mark.parametrize("split", [64, 1024, 4096, 16384])
+@pytest.mark.parametrize("split", [64, 1024, 4096, 16384, 32768])
 def test_decode_splits(split):
     ctx = [1, 63, 2049, 5000, 9000, 17000]
     say(f"decode split {split}: ctx {ctx}")
