@@ -1646,9 +1646,9 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
 
 // ---------------------------------------------------------------------------
 // a4 on MFMA: decode with D = 128 (decode_mfma_kernel<G>). One workgroup of
-// four waves runs one item (request, kv head, partition); the partition's
+// eight waves runs one item (request, kv head, partition); the partition's
 // 16-key tiles (one page each) go round-robin to the waves, tile t to wave
-// t % 4, and each wave keeps its own online-softmax state. Per tile and wave:
+// t % 8, and each wave keeps its own online-softmax state. Per tile and wave:
 //   K and V rows of the kv head reach the wave's LDS buffers by DMA (4 + 4
 //   instructions of 1 KB), NB buffers deep, counted waits;
 //   S^T = K Q^T: 4 v_mfma_f32_16x16x32_bf16, keys as M, the group's G q heads
@@ -1656,11 +1656,13 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
 //   online softmax per q head over the lanes n, n + 16, n + 32, n + 48;
 //   O^T += V^T P^T: 8 v_mfma_f32_16x16x16_bf16, P as the scores left it,
 //   V^T by transposing reads.
-// The four waves' states fold in ascending wave order (combine_sym), as in
+// The eight waves' states fold in ascending wave order (combine_sym), as in
 // decode_kernel. The page list of the partition is copied to LDS once, so the
 // tile loop holds no global load the compiler would count.
 // ---------------------------------------------------------------------------
-constexpr int kDecMfmaWaves = 4;
+// Waves per item: eight keep twice the tiles of a small batch in flight at the
+// same waves per CU as two four-wave workgroups (one workgroup per CU: LDS).
+constexpr int kDecMfmaWaves = 8;
 constexpr int kDecMfmaMaxPages = 1024;  // page list in LDS: splits up to 16384 keys
 constexpr int kDecMfmaBufs = 2;         // tile buffers per wave
 
@@ -1680,6 +1682,7 @@ __device__ __forceinline__ void dec_wait(int tiles_ahead) {
 }
 
 template <int G>
+// (a register budget of 128 VGPRs: the kernel takes 103)
 __global__ void __launch_bounds__(64 * kDecMfmaWaves, 2)
 decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
                    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -1835,7 +1838,7 @@ decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restric
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- fold the four waves' states in order (their buffers are free now) ----
+  // ---- fold the waves' states in order (their buffers are free now) ----
   const float l_row = quad_sum(lsum);
   __syncthreads();  // every wave is past its last tile
   float* sm_o = reinterpret_cast<float*>(&lds[0][0][0]);  // [wave][G][D]
