@@ -1645,16 +1645,16 @@ mla_decode_kernel(const WorkItem* __restrict__ items, int n_items,
 }
 
 // ---------------------------------------------------------------------------
-// a4 on MFMA: decode with D = 128 (decode_mfma_kernel<G>). One workgroup of
+// a4 on MFMA: decode (decode_mfma_kernel<D, G>, D = 64 or 128). One workgroup of
 // eight waves runs one item (request, kv head, partition); the partition's
 // 16-key tiles (one page each) go round-robin to the waves, tile t to wave
 // t % 8, and each wave keeps its own online-softmax state. Per tile and wave:
-//   K and V rows of the kv head reach the wave's LDS buffers by DMA (4 + 4
-//   instructions of 1 KB), NB buffers deep, counted waits;
-//   S^T = K Q^T: 4 v_mfma_f32_16x16x32_bf16, keys as M, the group's G q heads
-//   as N (16 columns, G of them real);
+//   K and V rows of the kv head reach the wave's LDS buffers by DMA (D / 32 +
+//   D / 32 instructions of 1 KB), NB buffers deep, counted waits;
+//   S^T = K Q^T: D / 32 v_mfma_f32_16x16x32_bf16, keys as M, the group's G q
+//   heads as N (16 columns, G of them real);
 //   online softmax per q head over the lanes n, n + 16, n + 32, n + 48;
-//   O^T += V^T P^T: 8 v_mfma_f32_16x16x16_bf16, P as the scores left it,
+//   O^T += V^T P^T: D / 16 v_mfma_f32_16x16x16_bf16, P as the scores left it,
 //   V^T by transposing reads.
 // The eight waves' states fold in ascending wave order (combine_sym), as in
 // decode_kernel. The page list of the partition is copied to LDS once, so the
@@ -1666,12 +1666,21 @@ constexpr int kDecMfmaWaves = 8;
 constexpr int kDecMfmaMaxPages = 1024;  // page list in LDS: splits up to 16384 keys
 constexpr int kDecMfmaBufs = 2;         // tile buffers per wave
 
-// Chunk permutation of tile row r (16 chunks of 16 bytes): chunk c sits at
-// slot c ^ f(r), f(r) = 2 (r % 8) + r / 8. The K reads (row n16, one chunk,
-// 16 rows per 16 lanes) then take 16 distinct slots of a 256-byte bank cycle,
-// and the transposing V reads (rows 4 g4 .. 4 g4 + 3, 32 bytes each, and any
-// 8 consecutive rows) take distinct 32-byte halves of it.
-__device__ __forceinline__ int dec_swz(int r) { return ((r & 7) << 1) | (r >> 3); }
+// Chunk permutation of tile row r: chunk c sits at slot c ^ f(r).
+// D = 128 (16 chunks of 16 bytes, a row per 256-byte bank cycle): f(r) =
+// 2 (r % 8) + r / 8. The K reads (row n16, one chunk, 16 rows per 16 lanes)
+// then take 16 distinct slots of the cycle, and the transposing V reads (rows
+// 4 g4 .. 4 g4 + 3, 32 bytes each, and any 8 consecutive rows) take distinct
+// 32-byte pairs of it.
+// D = 64 (8 chunks, two rows per cycle, rows of one parity share its banks):
+// f(r) = 2 ((r / 2) % 4) + r / 8, distinct over the 8 rows of each parity
+// (K reads), and its pair index (r / 2) % 4 distinct over the rows of equal
+// parity in any 4 or 8 consecutive rows (V reads).
+template <int D>
+__device__ __forceinline__ int dec_swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | (r >> 3);
+  else return (((r >> 1) & 3) << 1) | (r >> 3);
+}
 
 template <int N>
 __device__ __forceinline__ void dec_wait(int tiles_ahead) {
@@ -1681,8 +1690,8 @@ __device__ __forceinline__ void dec_wait(int tiles_ahead) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int G>
-// (a register budget of 128 VGPRs: the kernel takes 103)
+template <int D, int G>
+// (a register budget of 128 VGPRs: the kernel takes 103 at D = 128)
 __global__ void __launch_bounds__(64 * kDecMfmaWaves, 2)
 decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
                    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -1690,10 +1699,11 @@ decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restric
                    int num_kv_heads, int split, uint16_t* __restrict__ out,
                    float* __restrict__ lse_out, float* __restrict__ o_part,
                    float* __restrict__ lse_part) {
-  constexpr int D = 128;
   constexpr int RB = 2 * D;        // bytes of one key row of one head
-  constexpr int TB = 16 * RB;      // one tensor's tile: 16 keys, 4 KB
+  constexpr int TB = 16 * RB;      // one tensor's tile: 16 keys
   constexpr int NI = TB / 1024;    // DMA instructions per tensor tile
+  constexpr int RPI = 1024 / RB;   // rows per DMA instruction (4 or 8)
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row (16 or 8)
   constexpr int NS = D / 32;       // score k-steps
   constexpr int NV = D / 16;       // PV dim blocks
   constexpr int NB = kDecMfmaBufs;
@@ -1731,9 +1741,9 @@ decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restric
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // DMA of tile t into buffer b: tensor x, instruction i fills rows 4 i ..
-  // 4 i + 3 of the buffer's x half; lane l puts 16 bytes in slot l % 16 of
-  // row 4 i + l / 16, i.e. chunk (l % 16) ^ f(row) of that key's row. Keys
+  // DMA of tile t into buffer b: tensor x, instruction i fills rows RPI i ..
+  // RPI i + RPI - 1 of the buffer's x half; lane l puts 16 bytes in slot
+  // l % CPR of row RPI i + l / CPR, i.e. chunk (l % CPR) ^ f(row). Keys
   // past the partition read its last key (same page: tiles are page-aligned).
   const uint32_t lds_base = lds_offset(&lds[wave][0][0]);
   const int64_t slot_bytes = static_cast<int64_t>(num_kv_heads) * RB;
@@ -1748,21 +1758,21 @@ decode_mfma_kernel(const WorkItem* __restrict__ items, const uint16_t* __restric
       const uint8_t* base = reinterpret_cast<const uint8_t*>(x == 0 ? kp : vp) + page_bytes;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int r = 4 * i + (lane >> 4);
+        const int r = RPI * i + lane / CPR;
         const int key = min(t0 + r, last_key);
         const uint32_t off =
-            static_cast<uint32_t>((key & 15) * slot_bytes + 16 * ((lane & 15) ^ dec_swz(r)));
+            static_cast<uint32_t>((key & 15) * slot_bytes + 16 * ((lane % CPR) ^ dec_swz<D>(r)));
         lds_dma16_sbase(off, base, lds_base + b * (2 * TB) + x * TB + 1024 * i);
       }
     }
   };
 
   // K fragment s (A operand): key n16, dims 32 s + 8 g4 .., chunk 4 s + g4
-  const int fk = dec_swz(n16);
+  const int fk = dec_swz<D>(n16);
   // V^T fragment of dim block b: keys 4 g4 .. 4 g4 + 3 (row vr and the three
   // after it, transposed by the read), dims 16 b + 4 (n16 % 4) .. + 3
   const int vr = 4 * g4 + (n16 >> 2);
-  const int fv = dec_swz(vr);
+  const int fv = dec_swz<D>(vr);
 
   float m = kNegInf;
   float lsum = 0.0f;
@@ -2390,11 +2400,11 @@ void launch_decode(const ListLaunch& L, const uint16_t* q, const uint16_t* kp, c
                      L.num_qo_heads, L.num_kv_heads, L.split, out, lse, L.o_part, L.lse_part);
 }
 
-template <int G>
+template <int D, int G>
 void launch_decode_mfma(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
                         const uint16_t* vp, const int32_t* pt, float scale_log2, uint16_t* out,
                         float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mfma_kernel<G>), dim3(L.n), dim3(64 * kDecMfmaWaves), 0, stream,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(L.n), dim3(64 * kDecMfmaWaves), 0, stream,
                      reinterpret_cast<const WorkItem*>(L.items), q, kp, vp, pt, scale_log2,
                      L.num_qo_heads, L.num_kv_heads, L.split, out, lse, L.o_part, L.lse_part);
 }
@@ -2403,14 +2413,14 @@ template <int D>
 void launch_decode_g(const ListLaunch& L, const uint16_t* q, const uint16_t* kp,
                      const uint16_t* vp, const int32_t* pt, float scale_log2, uint16_t* out,
                      float* lse, hipStream_t stream) {
-  // D = 128 at splits the LDS page list holds: the MFMA decode (the choice
-  // depends on the head dim and the split only, never on the batch)
-  if (D == 128 && L.split <= 16 * kDecMfmaMaxPages) {
+  // splits the LDS page list holds: the MFMA decode (the choice depends on
+  // the split only, never on the batch)
+  if (L.split <= 16 * kDecMfmaMaxPages) {
     switch (L.group) {
-      case 1: launch_decode_mfma<1>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-      case 2: launch_decode_mfma<2>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-      case 4: launch_decode_mfma<4>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
-      default: launch_decode_mfma<8>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      case 1: launch_decode_mfma<D, 1>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      case 2: launch_decode_mfma<D, 2>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      case 4: launch_decode_mfma<D, 4>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
+      default: launch_decode_mfma<D, 8>(L, q, kp, vp, pt, scale_log2, out, lse, stream); break;
     }
     return;
   }
