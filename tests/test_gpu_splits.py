@@ -39,3 +39,15 @@ def test_decode_splits(split):
     b = W.decode_batch(len(ctx), ctx_lens=ctx, seed=31, num_pages=4096, device=DEV)
     out, lse = run_decode(b, split=split)
     assert_parity(out, lse, b, what=f"decode split {split}")
+
+
+@pytest.mark.parametrize("heads", [dict(num_qo_heads=16, num_kv_heads=2, head_dim=64),
+                                   dict(num_qo_heads=4, num_kv_heads=1, head_dim=64)],
+                         ids=["hq16_hkv2_d64", "hq4_hkv1_d64"])
+def test_decode_split_32768_head_dim_64(heads):
+    """head_dim 64 past the MFMA decode's page list: the VALU decode."""
+    ctx = [1, 63, 2049, 17000, 40000]
+    say(f"decode split 32768 {heads}: ctx {ctx}")
+    b = W.decode_batch(len(ctx), ctx_lens=ctx, seed=37, num_pages=8192, device=DEV, head=heads)
+    out, lse = run_decode(b, split=32768)
+    assert_parity(out, lse, b, what=f"decode split 32768 {heads}")
